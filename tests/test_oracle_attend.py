@@ -1,0 +1,82 @@
+"""Pins for the oracle's attention over a dequantized cache (no GPU).
+
+Checked against the textbook definition evaluated by torch in float64 (an independent
+library routine), and against special cases with closed forms: one key gives O = V,
+identical keys give O = mean(V), a dominant key selects its value row.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _f(h):
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _all_rows(tq, heads):
+    return np.arange(tq * heads, dtype=np.int64)
+
+
+def test_attend_vs_torch_float64():
+    rng = np.random.default_rng(21)
+    tq, tk, H, d = 7, 53, 3, 64
+    q = _bf16(rng.standard_normal((tq, H, d)) * 0.5).reshape(tq, H, d)
+    k = _bf16(rng.standard_normal((tk, H, d))).reshape(tk, H, d)
+    v = _bf16(rng.standard_normal((tk, H, d))).reshape(tk, H, d)
+    scale = 1.0 / np.sqrt(d)
+    got = _f(oracle.attend_rows(q, k, v, scale, _all_rows(tq, H))).reshape(tq, H, d)
+    Q, K, V = (torch.from_numpy(_f(t).astype(np.float64)).permute(1, 0, 2) for t in (q, k, v))
+    P = torch.softmax((Q @ K.transpose(1, 2)) * scale, dim=-1)
+    ref = (P @ V).permute(1, 0, 2).numpy()
+    # one bf16 rounding (plus a binary32 rounding) separates the two
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-12)
+
+
+def test_single_key_returns_value_row():
+    rng = np.random.default_rng(22)
+    q = _bf16(rng.standard_normal((5, 2, 128))).reshape(5, 2, 128)
+    k = _bf16(rng.standard_normal((1, 2, 128))).reshape(1, 2, 128)
+    v = _bf16(rng.standard_normal((1, 2, 128))).reshape(1, 2, 128)
+    got = oracle.attend_rows(q, k, v, 0.1, _all_rows(5, 2)).reshape(5, 2, 128)
+    for t in range(5):
+        assert np.array_equal(got[t], v[0])
+
+
+def test_identical_keys_average_values():
+    rng = np.random.default_rng(23)
+    tk = 40
+    q = _bf16(rng.standard_normal((3, 1, 64))).reshape(3, 1, 64)
+    k = np.repeat(_bf16(rng.standard_normal((1, 1, 64))).reshape(1, 1, 64), tk, axis=0)
+    v = _bf16(rng.standard_normal((tk, 1, 64))).reshape(tk, 1, 64)
+    got = _f(oracle.attend_rows(q, k, v, 1.0, _all_rows(3, 1))).reshape(3, 64)
+    mean = _f(v).astype(np.float64).mean(0)[0]
+    for t in range(3):
+        assert np.all(np.abs(got[t] - mean) <= np.abs(mean) * 2.0 ** -8 + 1e-12)
+
+
+def test_dominant_key_selects_its_value():
+    tk, d = 16, 64
+    k = np.zeros((tk, 1, d), np.float32)
+    k[5, 0, 0] = 1.0
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    v = np.random.default_rng(24).standard_normal((tk, 1, d)).astype(np.float32)
+    qb, kb, vb = _bf16(q).reshape(q.shape), _bf16(k).reshape(k.shape), _bf16(v).reshape(v.shape)
+    got = oracle.attend_rows(qb, kb, vb, 200.0, np.array([0], np.int64)).reshape(d)
+    assert np.array_equal(got, vb[5, 0])  # exp(-200) is far below half a bf16 ulp
+
+
+def test_row_subset_equals_full():
+    rng = np.random.default_rng(25)
+    tq, tk, H, d = 6, 20, 4, 64
+    q = _bf16(rng.standard_normal((tq, H, d))).reshape(tq, H, d)
+    k = _bf16(rng.standard_normal((tk, H, d))).reshape(tk, H, d)
+    v = _bf16(rng.standard_normal((tk, H, d))).reshape(tk, H, d)
+    full = oracle.attend_rows(q, k, v, 0.125, _all_rows(tq, H))
+    sub = np.array([3, 17, 22], np.int64)
+    assert np.array_equal(oracle.attend_rows(q, k, v, 0.125, sub), full[sub])
