@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""bench.py -- NVFP4 KV-cache quantize + dequantize throughput on one MI355X.
+
+One step of the default workload (the 30-layer full-cache read) is one pass of the whole
+hot path: quantize-on-append of the newest 4680-token chunk for every layer's K and V
+(group amax, block scales, E2M1 codes; mse rule) into its slab of the packed cache, then
+dequantization of the whole packed cache (30 layers x K,V x 32760 tokens x 12 heads x 128)
+to bf16.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is algorithmic bytes per step / time per step, where the
+bytes per element are bf16 (2) + codes (0.5) + scales (0.0625), plus 4 B per group amax.
+
+    python bench.py [--steps K] [--warmup W] [--config C3|C4|C2|C1] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV FP4 quant+dequant GB/s (bf16+packed bytes) and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0
+DEQUANT_SOURCE = os.path.join(ROOT, "kv_cache_fp4_amd", "csrc", "kvfp4.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C3", choices=["C1", "C2", "C3", "C4"])
+    ap.add_argument("--rule", default=None, choices=["static_6", "static_4", "mse"],
+                    help="append rule (default: mse for C3, static_6 otherwise)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args(argv)
+
+
+# ---- workload ---------------------------------------------------------------------------
+
+class CacheWorkload:
+    """Packed cache laid out as append slabs: [chunk][layer][K/V][tokens*heads rows][head_dim].
+    Group g = (chunk, layer, kv) in that order, so one chunk's append for every layer is one
+    contiguous quantize call and the whole cache is one contiguous dequantize call."""
+
+    def __init__(self, cfg, rule, device, keep_sources=False):
+        import torch
+
+        import kv_cache_fp4_amd as kv
+        import synth
+        self.cfg, self.rule, self.device = cfg, rule, device
+        D, rpg = cfg.head_dim, cfg.rows_per_group
+        self.rpg = rpg
+        self.slab_rows = cfg.groups_per_chunk * rpg
+        self.rows = cfg.chunks * self.slab_rows
+        self.n_groups = cfg.chunks * cfg.groups_per_chunk
+        self.codes = torch.empty((self.rows, D // 2), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((self.rows, D // 16), dtype=torch.uint8, device=device)
+        self.amax = torch.empty((self.n_groups,), dtype=torch.float32, device=device)
+        self.out = torch.empty((self.rows, D), dtype=torch.bfloat16, device=device)
+        self.sources = {}
+        for c in range(cfg.chunks):
+            src = synth.chunk_all_layers(cfg, c, device=device)
+            self.quantize_chunk(c, src)
+            if keep_sources or c == cfg.chunks - 1:
+                self.sources[c] = src
+            else:
+                del src
+        torch.cuda.synchronize(device)
+        self.append_src = self.sources[cfg.chunks - 1]
+        self.kv = kv
+
+    def slab(self, c):
+        r0, r1 = c * self.slab_rows, (c + 1) * self.slab_rows
+        g0, g1 = c * self.cfg.groups_per_chunk, (c + 1) * self.cfg.groups_per_chunk
+        return self.codes[r0:r1], self.scales[r0:r1], self.amax[g0:g1]
+
+    def quantize_chunk(self, c, src):
+        import kv_cache_fp4_amd as kv
+        codes, scales, amax = self.slab(c)
+        kv.kvfp4_quantize(src, self.rpg, self.rule, codes, scales, amax)
+
+    def append(self):
+        self.quantize_chunk(self.cfg.chunks - 1, self.append_src)
+
+    def dequantize_all(self):
+        self.kv.kvfp4_dequantize(self.codes, self.scales, self.amax, self.rpg, y=self.out)
+
+    @property
+    def append_elems(self):
+        return self.slab_rows * self.cfg.head_dim
+
+    @property
+    def cache_elems(self):
+        return self.rows * self.cfg.head_dim
+
+    def append_bytes(self):
+        return self.append_elems * BYTES_PER_ELEM + 4 * self.cfg.groups_per_chunk
+
+    def dequant_bytes(self):
+        return self.cache_elems * BYTES_PER_ELEM + 4 * self.n_groups
+
+
+# ---- CPU baseline (oracle, single thread) -----------------------------------------------
+
+def cpu_baseline(cfg, rule, budget_s=12.0):
+    """Time the oracle on a bounded sample with the step's byte mix: quantize one scale group
+    (one chunk of one tensor) with the step's rule, then dequantize it `chunks` times (the
+    whole-cache read is `chunks` times the append)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    x = synth.chunk_group(cfg, 0, 0, 0).reshape(-1, cfg.head_dim)
+    xh = x.view(__import__("torch").int16).numpy().view(np.uint16)
+    n = xh.size
+    t0 = time.perf_counter()
+    done_q = done_dq = 0
+    while True:
+        c, s, a = oracle.quantize(xh, cfg.rows_per_group, rule)
+        done_q += n
+        for _ in range(cfg.chunks):
+            oracle.dequantize(c, s, a, cfg.rows_per_group)
+            done_dq += n
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    gbs = (done_q + done_dq) * BYTES_PER_ELEM / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done_q // n} x (quantize one {cfg.chunk_tokens}x{cfg.heads}x{cfg.head_dim} "
+                       f"group, {rule}, then dequantize it {cfg.chunks} times) = {done_q} + "
+                       f"{done_dq} elements in {dt:.1f} s, single-threaded C oracle")}
+
+
+# ---- counters ----------------------------------------------------------------------------
+
+def _source_hash():
+    with open(DEQUANT_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_for(workload_name):
+    """HBM bytes per dequant launch from the committed counter summary, or None when the
+    summary is missing, is for another workload, or predates the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != _source_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("dequant_bytes_per_launch")
+
+
+# ---- main -----------------------------------------------------------------------------------
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
+              "dequantize path has no communication and the quantize path would need one "
+              "max-allreduce of the group amax per append -- see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    rule = args.rule or ("mse" if args.config == "C3" else "static_6")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: building {cfg.name} ({rule}) on {torch.cuda.get_device_name(dev)}", file=sys.stderr,
+          flush=True)
+    w = CacheWorkload(cfg, rule, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize(dev)
+
+    for _ in range(args.warmup):
+        w.append()
+        w.dequantize_all()
+    torch.cuda.synchronize(dev)
+    print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, end = ev(), ev()
+    dq = [(ev(), ev()) for _ in range(args.steps)]
+    ap = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    start.record(stream)
+    for i in range(args.steps):
+        ap[i][0].record(stream)
+        w.append()
+        ap[i][1].record(stream)
+        dq[i][0].record(stream)
+        w.dequantize_all()
+        dq[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    ms_dq = sum(a.elapsed_time(b) for a, b in dq) / args.steps
+    ms_ap = sum(a.elapsed_time(b) for a, b in ap) / args.steps
+
+    step_bytes = w.append_bytes() + w.dequant_bytes()
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    dq_gbs = w.dequant_bytes() / (ms_dq * 1e-3) / 1e9
+    ap_gbs = w.append_bytes() / (ms_ap * 1e-3) / 1e9
+    workload = (f"{cfg.name}: append one {cfg.chunk_tokens}-token chunk for {cfg.layers} layers x K,V "
+                f"({rule}) + dequantize the whole {cfg.cache_tokens}-token cache "
+                f"({cfg.layers} x 2 x {cfg.cache_tokens} x {cfg.heads} x {cfg.head_dim})")
+    traffic = traffic_for(cfg.name)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "layers": cfg.layers, "heads": cfg.heads,
+                   "head_dim": cfg.head_dim, "cache_tokens": cfg.cache_tokens,
+                   "chunk_tokens": cfg.chunk_tokens, "rule": rule,
+                   "elements_per_step": w.append_elems + w.cache_elems,
+                   "bytes_per_step": step_bytes, "generator_version": synth.GENERATOR_VERSION},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "dequant_kernel",
+                     "achieved": round(dq_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dq_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": w.dequant_bytes(), "ms_per_launch": round(ms_dq, 4)},
+        "breakdown": {"append_ms": round(ms_ap, 4), "append_GBps": round(ap_gbs, 2),
+                      "append_bytes": w.append_bytes(),
+                      "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, rule)
+        res["cpu_baseline"]["host_threads_available"] = os.cpu_count()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,124 @@
+/*
+ * kvfp4.h -- C ABI of libkvfp4: NVFP4 (E2M1 codes, E4M3 block scales, fp32 group amax)
+ * compression of a transformer KV cache on MI355X (gfx950).
+ *
+ * Pages cited (titles as published):
+ *   [P-KV]    "How to Use KV Cache Quantization with LongLive's LongLiveQuantizationConfig"
+ *   [P-NVFP4] "How NVFP4 Quantization Works in LongLive 2.0 for Transformer Inference"
+ *   [P-SF]    "KV Cache Quantization for Self-Forcing Video Generation: A 33-Method
+ *              Empirical Study"
+ *
+ * Packed format (one "scale group" = rows_per_group consecutive rows, e.g. one appended
+ * chunk of K or of V; row = one (token, head) vector of head_dim elements):
+ *   codes   uint8  [rows, head_dim/2]   two E2M1 codes per byte, element 2j in the low
+ *                                       nibble, 2j+1 in the high nibble; code bit 3 = sign
+ *   scales  uint8  [rows, head_dim/16]  one OCP FP8 E4M3 block scale per 16 consecutive
+ *                                       elements of a row (0x00..0x7E)
+ *   amax    float  [ceil(rows/rows_per_group)]  max |x| of each scale group
+ * That is 4.5 bits per element plus 4 bytes per group (3.56x smaller than bf16).
+ *
+ * Arithmetic (every step one IEEE binary32 operation, round to nearest even):
+ *   s_enc = A > 0 ? 2688/A : 0,  s_dec = A/2688          (2688 = e2m1_max 6 * e4m3_max 448)
+ *   per 16-element block with m = max|x|, for divisor Dv (6 for static_6, 4 for static_4):
+ *     sf = E4M3_RNE_SAT((m/Dv) * s_enc),  S = E4M3(sf) * s_dec,  inv = S > 0 ? 1/S : 0
+ *     code_i = sign(x_i*inv) | E2M1_RNE_SAT(|x_i*inv|)   (ties to even, saturate at 6)
+ *   mse: both candidates; err = fma-chain of (x_i - E2M1(c_i)*S)^2 over elements 0..7 plus
+ *        the chain over 8..15; the 4-max candidate wins only if its err is strictly lower.
+ *   dequantize: y_i = bf16_rne(E2M1(c_i) * (E4M3(sf) * (A/2688)))
+ *
+ * Conventions for every entry point:
+ *   - pointers are DEVICE pointers unless stated; the caller allocates and frees all of
+ *     them; the library never allocates, never synchronizes, keeps no state besides a
+ *     thread-local copy of the last HIP error, and is reentrant across streams;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work is only
+ *     enqueued, the call returns before it runs;
+ *   - argument errors are detected on the host and returned before anything is enqueued;
+ *     rows == 0 (or q_tokens == 0) is a no-op that returns KVFP4_OK;
+ *   - inputs and outputs must not overlap;
+ *   - no C++ exception crosses the ABI.
+ */
+#ifndef KVFP4_H
+#define KVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVFP4_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum kvfp4_status {
+  KVFP4_OK = 0,
+  KVFP4_EINVAL = 1,      /* null pointer with work to do, negative size, rows_per_group <= 0,
+                            unknown rule, size overflow */
+  KVFP4_EALIGN = 2,      /* a pointer is not aligned as its argument requires */
+  KVFP4_EUNSUPPORTED = 3,/* head_dim not a multiple of 64 in [64, 1024] (attend: 64 or 128) */
+  KVFP4_EHIP = 4         /* a kernel launch failed; kvfp4_last_hip_error() has the code;
+                            outputs are undefined */
+};
+
+/* Block-scale rules: [P-KV] "Programmatic Configuration" and "Configuration Parameters
+ * Reference" (static_6 default; static_4 and mse alternatives). */
+enum kvfp4_rule {
+  KVFP4_RULE_STATIC6 = 0, /* block amax mapped to 6: scale = amax/6 ([P-NVFP4] "Understanding
+                             the NVFP4 Format and Architecture") */
+  KVFP4_RULE_STATIC4 = 1, /* block amax mapped to 4 */
+  KVFP4_RULE_MSE = 2      /* per block, whichever of the two has the lower squared error */
+};
+
+/*
+ * kvfp4_quantize -- quantize-on-append of K or V blocks.
+ * [P-KV] "FP4 Quantization in the Causal Model" (each key and value block is compressed
+ * independently on write); [P-NVFP4] "Stage 1" (per-block amax, per-block scale, two codes
+ * per uint8, one global amax per tensor) and "Stage 3" (global scale formula);
+ * [P-SF] Table 3 (blockwise, block size 16, quantize on write).
+ *
+ *   x               bf16 bit patterns [rows, head_dim], row-major; 16-byte aligned
+ *   rows            number of rows (>= 0)
+ *   head_dim        elements per row: a multiple of 64 in [64, 1024]
+ *   rows_per_group  rows per scale group (> 0); group g = rows [g*rpg, min((g+1)*rpg, rows))
+ *   rule            enum kvfp4_rule
+ *   codes   (out)   uint8 [rows, head_dim/2]; 16-byte aligned
+ *   scales  (out)   uint8 [rows, head_dim/16]; 4-byte aligned
+ *   group_amax (out) float [ceil(rows/rows_per_group)]; 4-byte aligned
+ * Appending a chunk to a cache = passing pointers offset to the chunk's first row and
+ * group.  Inputs must be finite.  Enqueues three kernels (amax clear, group amax, encode).
+ */
+int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
+                   int32_t rule, uint8_t* codes, uint8_t* scales, float* group_amax,
+                   void* stream);
+
+/*
+ * kvfp4_dequantize -- reconstruct bf16 K/V from the packed cache before attention.
+ * [P-KV] "CUDA De-quantization Pipeline" (bf16 reconstruction of the cache before
+ * attention); [P-NVFP4] "Stage 3" (each byte expands to two 4-bit values multiplied by the
+ * per-block and the global scale; bf16 output); [P-SF] Table 3 (the active cache is
+ * dequantized back to dense BF16 before attention).
+ *
+ *   codes, scales, group_amax   as written by kvfp4_quantize (same alignment rules)
+ *   rows, head_dim, rows_per_group   as for kvfp4_quantize
+ *   y      (out)   bf16 bit patterns [rows, head_dim]; 16-byte aligned
+ * One kernel launch for any number of rows and groups (64-bit indexing).
+ */
+int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
+                     int64_t rows, int32_t head_dim, int64_t rows_per_group, uint16_t* y,
+                     void* stream);
+
+/* Host-side size helper: bytes of codes and scales and the number of group amax floats
+ * for a tensor of `rows` rows.  Returns KVFP4_EINVAL / KVFP4_EUNSUPPORTED like the calls
+ * above.  Any output pointer may be NULL. */
+int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
+                       int64_t* codes_bytes, int64_t* scales_bytes, int64_t* n_groups);
+
+/* Diagnostics. */
+const char* kvfp4_status_str(int status); /* static string, never NULL */
+int kvfp4_abi_version(void);              /* KVFP4_ABI_VERSION */
+int kvfp4_last_hip_error(void);           /* hipError_t of this thread's last failed launch */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFP4_H */

@@ -1,0 +1,129 @@
+"""kv_cache_fp4_amd -- NVFP4 KV-cache compression for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libkvfp4.so`` (declared in ``include/kvfp4.h``).
+The functions below have the same names as the C entry points and only marshal
+arguments: tensor pointers, sizes and the caller's HIP stream.  torch supplies device
+memory and streams; every step of the computation runs in the HIP kernels.  There is no
+fallback: if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime (libamdhip64.so.7 with an $ORIGIN rpath).  Importing it
+# first makes this library bind to that same runtime instead of loading a second copy from
+# /opt/rocm, which would give the process two HIP runtimes with separate device contexts.
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvfp4.so")
+
+RULES = {"static_6": 0, "static_4": 1, "mse": 2}
+
+KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_EHIP = range(5)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libkvfp4.so not found at {LIB_PATH}; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.kvfp4_quantize.argtypes = [P, i64, i32, i64, i32, P, P, P, P]
+    L.kvfp4_quantize.restype = ctypes.c_int
+    L.kvfp4_dequantize.argtypes = [P, P, P, i64, i32, i64, P, P]
+    L.kvfp4_dequantize.restype = ctypes.c_int
+    L.kvfp4_packed_sizes.argtypes = [i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64)]
+    L.kvfp4_packed_sizes.restype = ctypes.c_int
+    L.kvfp4_status_str.argtypes = [ctypes.c_int]
+    L.kvfp4_status_str.restype = ctypes.c_char_p
+    L.kvfp4_abi_version.argtypes = []
+    L.kvfp4_abi_version.restype = ctypes.c_int
+    L.kvfp4_last_hip_error.argtypes = []
+    L.kvfp4_last_hip_error.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+class KVFP4Error(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = lib.kvfp4_status_str(status).decode()
+        if status == KVFP4_EHIP:
+            msg += f" (hipError {lib.kvfp4_last_hip_error()})"
+        super().__init__(msg)
+
+
+def _check(rc: int) -> None:
+    if rc != KVFP4_OK:
+        raise KVFP4Error(rc)
+
+
+def _rule(rule) -> int:
+    return RULES[rule] if isinstance(rule, str) else int(rule)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("kvfp4: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def kvfp4_packed_sizes(rows: int, head_dim: int, rows_per_group: int):
+    """(codes_bytes, scales_bytes, n_groups) for a tensor of `rows` rows."""
+    c, s, g = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.kvfp4_packed_sizes(rows, head_dim, rows_per_group, ctypes.byref(c),
+                                  ctypes.byref(s), ctypes.byref(g)))
+    return c.value, s.value, g.value
+
+
+def kvfp4_quantize(x, rows_per_group: int, rule="static_6", codes=None, scales=None,
+                   group_amax=None, stream=None):
+    """Quantize bf16 rows ``x`` [..., head_dim] (contiguous, on the GPU).
+
+    Returns (codes uint8 [rows, head_dim/2], scales uint8 [rows, head_dim/16],
+    group_amax float32 [n_groups]); outputs that are passed in are written in place
+    (e.g. views into a cache at the appended chunk's rows)."""
+    import torch
+    head_dim = x.shape[-1]
+    rows = x.numel() // head_dim if head_dim else 0
+    cb, sb, ng = kvfp4_packed_sizes(rows, head_dim, rows_per_group)
+    if codes is None:
+        codes = torch.empty((rows, head_dim // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, head_dim // 16), dtype=torch.uint8, device=x.device)
+    if group_amax is None:
+        group_amax = torch.empty((ng,), dtype=torch.float32, device=x.device)
+    _check(lib.kvfp4_quantize(_ptr(x), rows, head_dim, rows_per_group, _rule(rule), _ptr(codes),
+                              _ptr(scales), _ptr(group_amax), _stream(stream, x.device)))
+    return codes, scales, group_amax
+
+
+def kvfp4_dequantize(codes, scales, group_amax, rows_per_group: int, y=None, stream=None):
+    """Dequantize a packed tensor to bf16 [rows, head_dim] (written into ``y`` if given)."""
+    import torch
+    rows = codes.shape[0]
+    head_dim = codes.shape[1] * 2 if codes.dim() == 2 else 0
+    if y is None:
+        y = torch.empty((rows, head_dim), dtype=torch.bfloat16, device=codes.device)
+    _check(lib.kvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(group_amax), rows, head_dim,
+                                rows_per_group, _ptr(y), _stream(stream, codes.device)))
+    return y
+
+
+__all__ = ["kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
+           "lib", "LIB_PATH"]

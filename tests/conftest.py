@@ -6,6 +6,8 @@
 import os
 import sys
 
+import torch  # noqa: F401  (load torch's HIP runtime before any native library of ours)
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

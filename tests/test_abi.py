@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function its header
+declares, and rejects bad arguments on the host before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_fp4_amd as kv
+from kv_cache_fp4_amd import (KVFP4_EALIGN, KVFP4_EINVAL, KVFP4_EUNSUPPORTED, KVFP4_OK, lib)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            txt = open(os.path.join(inc, f)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(kvfp4_\w+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "kvfp4_status_str",
+            "kvfp4_abi_version", "kvfp4_last_hip_error"} <= set(names)
+    raw = ctypes.CDLL(kv.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert lib.kvfp4_abi_version() == 1
+    for s in range(5):
+        assert lib.kvfp4_status_str(s)
+    assert b"unknown" in lib.kvfp4_status_str(99)
+
+
+A16 = 1 << 20  # a fake, 16-byte aligned address: validation never dereferences it
+
+
+def q(x=A16, rows=64, d=128, rpg=64, rule=0, codes=A16, scales=A16, amax=A16):
+    return lib.kvfp4_quantize(x, rows, d, rpg, rule, codes, scales, amax, None)
+
+
+def dq(codes=A16, scales=A16, amax=A16, rows=64, d=128, rpg=64, y=A16):
+    return lib.kvfp4_dequantize(codes, scales, amax, rows, d, rpg, y, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), KVFP4_EINVAL),
+    (dict(rpg=0), KVFP4_EINVAL),
+    (dict(rpg=-5), KVFP4_EINVAL),
+    (dict(rule=3), KVFP4_EINVAL),
+    (dict(rule=-1), KVFP4_EINVAL),
+    (dict(x=None), KVFP4_EINVAL),
+    (dict(codes=None), KVFP4_EINVAL),
+    (dict(scales=None), KVFP4_EINVAL),
+    (dict(amax=None), KVFP4_EINVAL),
+    (dict(d=48), KVFP4_EUNSUPPORTED),
+    (dict(d=96), KVFP4_EUNSUPPORTED),
+    (dict(d=2048), KVFP4_EUNSUPPORTED),
+    (dict(d=0), KVFP4_EUNSUPPORTED),
+    (dict(x=A16 + 8), KVFP4_EALIGN),
+    (dict(codes=A16 + 4), KVFP4_EALIGN),
+    (dict(scales=A16 + 2), KVFP4_EALIGN),
+    (dict(amax=A16 + 2), KVFP4_EALIGN),
+    (dict(rows=1 << 50), KVFP4_EINVAL),
+])
+def test_quantize_rejects(kw, want):
+    assert q(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-3), KVFP4_EINVAL),
+    (dict(rpg=0), KVFP4_EINVAL),
+    (dict(codes=None), KVFP4_EINVAL),
+    (dict(y=None), KVFP4_EINVAL),
+    (dict(d=16), KVFP4_EUNSUPPORTED),
+    (dict(y=A16 + 2), KVFP4_EALIGN),
+    (dict(codes=A16 + 1), KVFP4_EALIGN),
+    (dict(scales=A16 + 1), KVFP4_EALIGN),
+])
+def test_dequantize_rejects(kw, want):
+    assert dq(**kw) == want
+
+
+def test_zero_rows_is_a_noop_even_with_null_pointers():
+    assert q(rows=0, x=None, codes=None, scales=None, amax=None) == KVFP4_OK
+    assert dq(rows=0, codes=None, scales=None, amax=None, y=None) == KVFP4_OK
+
+
+def test_packed_sizes():
+    assert kv.kvfp4_packed_sizes(56160 * 2, 128, 56160) == (56160 * 2 * 64, 56160 * 2 * 8, 2)
+    assert kv.kvfp4_packed_sizes(37, 64, 10) == (37 * 32, 37 * 4, 4)
+    assert kv.kvfp4_packed_sizes(0, 64, 10) == (0, 0, 0)
+    with pytest.raises(kv.KVFP4Error):
+        kv.kvfp4_packed_sizes(10, 80, 10)
