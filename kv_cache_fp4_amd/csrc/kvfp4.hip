@@ -32,12 +32,20 @@
 namespace kvfp4 {
 namespace {
 
-constexpr int kThreads = 256;           // 4 waves of 64
+constexpr int kThreads = 256;           // amax / encode workgroups: 4 waves of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kDequantUnroll = 4;
 constexpr int kQuantUnroll = 2;
 constexpr int kAmaxUnroll = 4;
 constexpr int64_t kTargetWorkgroups = 4096;  // 16 per CU on 256 CUs
+
+// Dequantize: many short workgroups of 2 waves, each wave writing one contiguous 2 KiB
+// run (2 x 1 KiB stores per lane group) with non-temporal stores.  Workgroups are
+// dispatched in index order, so the set of addresses being written at any moment is a
+// compact window of the output; measured on MI355X this beats persistent or longer
+// workgroups by 10-40% on the 7.7 GB whole-cache read (6.6 TB/s vs 4.6-6.0 TB/s).
+constexpr int kDqThreads = 128;
+constexpr int kDqUnroll = 2;
+constexpr int64_t kDqTileUnits = kDqThreads * kDqUnroll;  // 256 units = 2048 elements
 
 // Flat partition of a tensor into (group, slice) workgroups; sizes in 8-element units.
 struct Part {
@@ -212,28 +220,34 @@ __device__ __forceinline__ uint4 decode8(uint32_t w, float S) {
   return o;
 }
 
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales,
-                                                           const float* __restrict__ amax,
-                                                           uint4* __restrict__ y, Part p) {
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, (u32x4*)p);
+}
+
+// One tile of kDqTileUnits units per workgroup (the partition's slices are exactly one
+// tile; a group's last slice may be shorter).
+__global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ amax,
+                                                             uint4* __restrict__ y, Part p) {
   const Range r = wg_range(p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float s_dec = amax[r.g] / kGlobalDiv;
-  for (int64_t base = r.beg + wave * 64 * kDequantUnroll; base < r.end;
-       base += kWaves * 64 * kDequantUnroll) {
-    uint32_t c[kDequantUnroll], sf[kDequantUnroll];
+  const int64_t base = r.beg + wave * 64 * kDqUnroll;
+  uint32_t c[kDqUnroll], sf[kDqUnroll];
 #pragma unroll
-    for (int k = 0; k < kDequantUnroll; ++k) {
-      const int64_t u = base + k * 64 + lane;
-      const bool ok = u < r.end;
-      c[k] = ok ? codes[u] : 0u;
-      sf[k] = ok ? (uint32_t)scales[u >> 1] : 0u;
-    }
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t u = base + k * 64 + lane;
+    const bool ok = u < r.end;
+    c[k] = ok ? codes[u] : 0u;
+    sf[k] = ok ? (uint32_t)scales[u >> 1] : 0u;
+  }
 #pragma unroll
-    for (int k = 0; k < kDequantUnroll; ++k) {
-      const int64_t u = base + k * 64 + lane;
-      if (u < r.end) y[u] = decode8(c[k], e4m3_decode(sf[k]) * s_dec);
-    }
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t u = base + k * 64 + lane;
+    if (u < r.end) store_nt(y + u, decode8(c[k], e4m3_decode(sf[k]) * s_dec));
   }
 }
 
@@ -243,9 +257,11 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Shared argument checks; fills the partition on success.
-int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t unit_multiple, Part* part,
-         int64_t* n_groups) {
+// Shared argument checks; fills the partition on success.  fixed_slice > 0 makes every
+// slice exactly that many units (one tile per workgroup); otherwise slices are sized so
+// that about kTargetWorkgroups workgroups cover the tensor, rounded to unit_multiple.
+int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t unit_multiple, int64_t fixed_slice,
+         Part* part, int64_t* n_groups) {
   if (rows < 0 || rpg <= 0) return KVFP4_EINVAL;
   if (head_dim < 64 || head_dim > 1024 || head_dim % 64 != 0) return KVFP4_EUNSUPPORTED;
   const int64_t upr = head_dim / 8;  // units per row
@@ -253,10 +269,15 @@ int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t unit_multiple, Par
   const int64_t ng = rows == 0 ? 0 : (rows - 1) / rpg + 1;
   const int64_t rpg_eff = rpg < rows ? rpg : (rows > 0 ? rows : 1);
   const int64_t upg = rpg_eff * upr;
-  int64_t spg = (kTargetWorkgroups + ng - 1) / (ng > 0 ? ng : 1);
-  int64_t slice = (upg + spg - 1) / spg;
-  slice = (slice + unit_multiple - 1) / unit_multiple * unit_multiple;
-  spg = (upg + slice - 1) / slice;
+  int64_t slice;
+  if (fixed_slice > 0) {
+    slice = fixed_slice;
+  } else {
+    const int64_t want = (kTargetWorkgroups + ng - 1) / (ng > 0 ? ng : 1);
+    slice = (upg + want - 1) / want;
+    slice = (slice + unit_multiple - 1) / unit_multiple * unit_multiple;
+  }
+  const int64_t spg = (upg + slice - 1) / slice;
   if (ng * spg > INT32_MAX) return KVFP4_EINVAL;
   part->units_total = rows * upr;
   part->units_per_group = upg;
@@ -287,7 +308,7 @@ extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
     return KVFP4_EINVAL;
   Part part;
   int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, &part, &ng);
+  int rc = plan(rows, head_dim, rows_per_group, 64, 0, &part, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!x || !codes || !scales || !group_amax) return KVFP4_EINVAL;
@@ -324,14 +345,14 @@ extern "C" int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                 int64_t rows_per_group, uint16_t* y, void* stream) {
   Part part;
   int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, &part, &ng);
+  int rc = plan(rows, head_dim, rows_per_group, 64, kDqTileUnits, &part, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!codes || !scales || !group_amax || !y) return KVFP4_EINVAL;
   if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4) || !aligned(y, 16))
     return KVFP4_EALIGN;
   const unsigned grid = (unsigned)(ng * part.slices_per_group);
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, (hipStream_t)stream,
                      (const uint32_t*)codes, scales, group_amax, (uint4*)y, part);
   return launched();
 }
@@ -341,7 +362,7 @@ extern "C" int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_p
                                   int64_t* n_groups) {
   Part part;
   int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, &part, &ng);
+  int rc = plan(rows, head_dim, rows_per_group, 64, 0, &part, &ng);
   if (rc != KVFP4_OK) return rc;
   if (codes_bytes) *codes_bytes = rows * (head_dim / 2);
   if (scales_bytes) *scales_bytes = rows * (head_dim / 16);
