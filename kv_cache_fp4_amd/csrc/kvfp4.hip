@@ -7,22 +7,25 @@
 //   [P-SF]    "KV Cache Quantization for Self-Forcing Video Generation: A 33-Method
 //              Empirical Study"
 //
-// Work decomposition.  All three streaming kernels see a tensor as a flat sequence of
-// 8-element "units" (16 B of bf16, 4 B of codes, half a 16-element scale block).  A scale
-// group (rows_per_group rows) is a contiguous run of units, and the grid is
-// n_groups x slices_per_group workgroups: workgroup (g, s) owns a contiguous slice of
-// group g.  Every workgroup therefore has one group amax, read once into a uniform
-// register, and never needs a per-lane division to find its group.  Inside a slice each
-// wave of 64 lanes takes 64*UNR consecutive units per step; the k-th load/store of a step
-// covers 64 consecutive units, so every wave instruction touches one contiguous span
-// (1 KiB of bf16, 256 B of codes, 32 B of scales).  Index math is 64-bit throughout.
+// Work decomposition.  The streaming kernels see a tensor as a flat sequence of 8-element
+// "units" (16 B of bf16, 4 B of codes, half of a 16-element scale block).  A scale group
+// (rows_per_group rows) is a contiguous run of units.  Each kernel cuts every group into
+// fixed-size slices of its own tile size and launches one workgroup per (group, slice),
+// in group-major order.  So a workgroup has a single group amax, read once into a
+// uniform register, and never divides per lane to find its group; and because workgroups
+// are dispatched in index order, the addresses in flight at any moment form a compact
+// window of the tensor, which is what lets these kernels run near the HBM limit on
+// MI355X (measured: persistent workgroups with long slices were 10-40% slower).
+// Within a slice each wave takes 64*UNR consecutive units per step and its k-th load or
+// store covers 64 consecutive units, so every wave instruction touches one contiguous
+// span (1 KiB of bf16, 256 B of codes).  Index math is 64-bit.
 //
-// Quantize (per [P-NVFP4] "Stage 1"): (1) clear the group amax words, (2) group amax by a
-// max over 15-bit bf16 magnitude patterns, one atomicMax per workgroup, (3) encode: two
-// lanes per 16-element block exchange their half-block amax through DPP, both derive the
-// same E4M3 scale, and each packs its 8 codes into one dword.
-// Dequantize (per [P-NVFP4] "Stage 3"): one pass, each lane turns one code dword and one
-// scale byte into 8 bf16 (one 16 B store).
+// Quantize ([P-NVFP4] "Stage 1"): (1) clear the group amax words, (2) group amax as a max
+// over 15-bit bf16 magnitude patterns with one atomicMax per workgroup, (3) encode: the two
+// lanes holding the halves of a 16-element block exchange half-block maxima through DPP,
+// both derive the same E4M3 scale, and each packs its 8 codes into one dword.
+// Dequantize ([P-NVFP4] "Stage 3"): one pass; each lane turns one code dword and one scale
+// byte into 8 bf16 (one 16 B non-temporal store).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,20 +35,16 @@
 namespace kvfp4 {
 namespace {
 
-constexpr int kThreads = 256;           // amax / encode workgroups: 4 waves of 64
-constexpr int kWaves = kThreads / 64;
-constexpr int kQuantUnroll = 2;
-constexpr int kAmaxUnroll = 4;
-constexpr int64_t kTargetWorkgroups = 4096;  // 16 per CU on 256 CUs
+// Launch shapes (threads per workgroup, units per lane per step, steps per workgroup),
+// chosen by sweeping on MI355X over the 30-layer cache shapes.
+constexpr int kAmaxThreads = 512, kAmaxUnroll = 4, kAmaxSteps = 4;
+constexpr int kQuantThreads = 128, kQuantUnroll = 2, kQuantSteps = 1;  // static rules
+constexpr int kMseThreads = 256, kMseUnroll = 2, kMseSteps = 4;        // mse rule
+constexpr int kDqThreads = 128, kDqUnroll = 2;                         // one step
 
-// Dequantize: many short workgroups of 2 waves, each wave writing one contiguous 2 KiB
-// run (2 x 1 KiB stores per lane group) with non-temporal stores.  Workgroups are
-// dispatched in index order, so the set of addresses being written at any moment is a
-// compact window of the output; measured on MI355X this beats persistent or longer
-// workgroups by 10-40% on the 7.7 GB whole-cache read (6.6 TB/s vs 4.6-6.0 TB/s).
-constexpr int kDqThreads = 128;
-constexpr int kDqUnroll = 2;
-constexpr int64_t kDqTileUnits = kDqThreads * kDqUnroll;  // 256 units = 2048 elements
+constexpr int64_t tile_units(int threads, int unroll, int steps) {
+  return (int64_t)threads * unroll * steps;
+}
 
 // Flat partition of a tensor into (group, slice) workgroups; sizes in 8-element units.
 struct Part {
@@ -79,21 +78,29 @@ __device__ __forceinline__ float swap_pair(float v) {
   return __uint_as_float(swap_pair(__float_as_uint(v)));
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, (u32x4*)p);
+}
+
 // ---- kernel 1: clear group amax ---------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * kThreads)
+__global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = 0u;
 }
 
 // ---- kernel 2: group amax ([P-NVFP4] "Stage 1", global amax scalar) ---------------------
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x,
-                                                        uint32_t* __restrict__ amax_bits, Part p) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restrict__ x,
+                                                            uint32_t* __restrict__ amax_bits,
+                                                            Part p) {
+  constexpr int kW = kAmaxThreads / 64;
   const Range r = wg_range(p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t mx = 0;
   for (int64_t base = r.beg + wave * 64 * kAmaxUnroll; base < r.end;
-       base += kWaves * 64 * kAmaxUnroll) {
+       base += kAmaxThreads * kAmaxUnroll) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
     for (int k = 0; k < kAmaxUnroll; ++k) {
@@ -105,19 +112,56 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-  __shared__ uint32_t red[kWaves];
+  __shared__ uint32_t red[kW];
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   if (threadIdx.x == 0 && r.beg < r.end) {
     uint32_t m = red[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = max(m, red[w]);
+    for (int w = 1; w < kW; ++w) m = max(m, red[w]);
     // A non-negative binary32 orders like its bit pattern; bf16 -> fp32 is a 16-bit shift.
     atomicMax(&amax_bits[r.g], m << 16);
   }
 }
 
 // ---- kernel 3: encode ([P-NVFP4] "Stage 1"; [P-KV] scale rules) -------------------------
+
+// Per-workgroup tables that replace the per-block divisions with lookups of values computed
+// by the very same binary32 operations (so results are bit-identical):
+//   t6[k]  = (128 + k) / 6          m/6 for a bf16 m with mantissa k, before the 2^e scaling
+//   S[sf]  = E4M3(sf) * s_dec       decoded block scale
+//   inv[sf] = S > 0 ? 1 / S : 0     its reciprocal
+struct Tables {
+  float t6[128], S[128], inv[128];
+};
+
+__device__ __forceinline__ void init_tables(Tables* tb, float s_dec, int nthreads) {
+  for (int i = threadIdx.x; i < 128; i += nthreads) {
+    tb->t6[i] = (float)(128 + i) / 6.0f;
+    const float S = e4m3_decode((uint32_t)i) * s_dec;
+    tb->S[i] = S;
+    tb->inv[i] = (S > 0.0f) ? 1.0f / S : 0.0f;
+  }
+  __syncthreads();
+}
+
+// t = m / Dv for a block amax m given as its bf16 magnitude pattern mb.
+// Dv = 4: m * 0.25 is the correctly rounded quotient.  Dv = 6: for a normal m with biased
+// exponent e8 >= 4 the quotient is t6[mantissa] * 2^(e8 - 134) exactly (the power-of-two
+// scaling is an exponent add that stays in the normal range); zero gives zero; the few
+// remaining tiny values take a real division.
+template <int DV>
+__device__ __forceinline__ float block_t(uint32_t mb, const Tables* tb) {
+  const float m = __uint_as_float(mb << 16);
+  if constexpr (DV == 4) {
+    return m * 0.25f;
+  } else {
+    const uint32_t e8 = mb >> 7;
+    float t = __uint_as_float(__float_as_uint(tb->t6[mb & 127u]) + ((e8 - 134u) << 23));
+    if (__builtin_expect(e8 < 4u, 0)) t = (mb == 0u) ? 0.0f : m / 6.0f;
+    return t;
+  }
+}
 
 // One candidate scaling of a block for this lane's 8 elements.
 struct Cand {
@@ -126,14 +170,14 @@ struct Cand {
   uint32_t codes;  // 8 packed E2M1 codes
 };
 
-__device__ __forceinline__ Cand make_cand(const float xf[8], float m, float dv, float s_enc,
-                                          float s_dec) {
+template <int DV>
+__device__ __forceinline__ Cand make_cand(const float xf[8], uint32_t mb, float s_enc,
+                                          const Tables* tb) {
   Cand c;
-  const float t = m / dv;   // IEEE division (correctly rounded)
-  const float u = t * s_enc;
+  const float u = block_t<DV>(mb, tb) * s_enc;
   c.sf = e4m3_encode(u);
-  c.S = e4m3_decode(c.sf) * s_dec;
-  const float inv = (c.S > 0.0f) ? 1.0f / c.S : 0.0f;
+  c.S = tb->S[c.sf];
+  const float inv = tb->inv[c.sf];
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = xf[i] * inv;
@@ -143,8 +187,8 @@ __device__ __forceinline__ Cand make_cand(const float xf[8], float m, float dv, 
 
 // Squared error of this lane's half block: fma chain in element order from +0.
 __device__ __forceinline__ float half_err(const float xf[8], const Cand& c) {
-  f32x2 v[4] = {e2m1_decode2<0>(c.codes), e2m1_decode2<1>(c.codes), e2m1_decode2<2>(c.codes),
-                e2m1_decode2<3>(c.codes)};
+  const f32x2 v[4] = {e2m1_decode2<0>(c.codes), e2m1_decode2<1>(c.codes),
+                      e2m1_decode2<2>(c.codes), e2m1_decode2<3>(c.codes)};
   float e = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -156,43 +200,42 @@ __device__ __forceinline__ float half_err(const float xf[8], const Cand& c) {
   return e;
 }
 
-template <int RULE>
-__global__ __launch_bounds__(kThreads) void quant_kernel(const uint4* __restrict__ x,
-                                                         const float* __restrict__ amax,
-                                                         uint32_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales, Part p) {
+template <int RULE, int THREADS, int UNR>
+__global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict__ x,
+                                                        const float* __restrict__ amax,
+                                                        uint32_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, Part p) {
   const Range r = wg_range(p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float A = amax[r.g];
   const float s_enc = (A > 0.0f) ? kGlobalDiv / A : 0.0f;
-  const float s_dec = A / kGlobalDiv;
-  for (int64_t base = r.beg + wave * 64 * kQuantUnroll; base < r.end;
-       base += kWaves * 64 * kQuantUnroll) {
-    uint4 v[kQuantUnroll];
+  __shared__ Tables tabs;
+  init_tables(&tabs, A / kGlobalDiv, THREADS);
+  for (int64_t base = r.beg + wave * 64 * UNR; base < r.end; base += THREADS * UNR) {
+    uint4 v[UNR];
 #pragma unroll
-    for (int k = 0; k < kQuantUnroll; ++k) {
+    for (int k = 0; k < UNR; ++k) {
       const int64_t u = base + k * 64 + lane;
       v[k] = (u < r.end) ? x[u] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < kQuantUnroll; ++k) {
+    for (int k = 0; k < UNR; ++k) {
       const int64_t u = base + k * 64 + lane;
-      float xf[8] = {bf16_lo(v[k].x), bf16_hi(v[k].x), bf16_lo(v[k].y), bf16_hi(v[k].y),
-                     bf16_lo(v[k].z), bf16_hi(v[k].z), bf16_lo(v[k].w), bf16_hi(v[k].w)};
+      const float xf[8] = {bf16_lo(v[k].x), bf16_hi(v[k].x), bf16_lo(v[k].y), bf16_hi(v[k].y),
+                           bf16_lo(v[k].z), bf16_hi(v[k].z), bf16_lo(v[k].w), bf16_hi(v[k].w)};
       // Block amax: this lane's 8 elements, then the partner lane's (the two lanes of a
       // pair hold the two halves of one 16-element block; all lanes execute the swap).
       uint32_t mb = absmax8_bits(v[k]);
       mb = max(mb, swap_pair(mb));
-      const float m = __uint_as_float(mb << 16);
       Cand pick;
       if constexpr (RULE == KVFP4_RULE_STATIC6) {
-        pick = make_cand(xf, m, 6.0f, s_enc, s_dec);
+        pick = make_cand<6>(xf, mb, s_enc, &tabs);
       } else if constexpr (RULE == KVFP4_RULE_STATIC4) {
-        pick = make_cand(xf, m, 4.0f, s_enc, s_dec);
+        pick = make_cand<4>(xf, mb, s_enc, &tabs);
       } else {
-        const Cand c6 = make_cand(xf, m, 6.0f, s_enc, s_dec);
-        const Cand c4 = make_cand(xf, m, 4.0f, s_enc, s_dec);
-        // err = (chain over elements 0..7) + (chain over 8..15); the sum of two values is
+        const Cand c6 = make_cand<6>(xf, mb, s_enc, &tabs);
+        const Cand c4 = make_cand<4>(xf, mb, s_enc, &tabs);
+        // err = (chain over elements 0..7) + (chain over 8..15); a sum of two values is
         // the same in either operand order, so both lanes of the pair agree.
         const float h6 = half_err(xf, c6), h4 = half_err(xf, c4);
         const float err6 = h6 + swap_pair(h6);
@@ -200,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const uint4* __restrict
         pick = (err4 < err6) ? c4 : c6;
       }
       if (u < r.end) {
-        codes[u] = pick.codes;
+        __builtin_nontemporal_store(pick.codes, codes + u);
         if ((lane & 1) == 0) scales[u >> 1] = (uint8_t)pick.sf;
       }
     }
@@ -220,14 +263,7 @@ __device__ __forceinline__ uint4 decode8(uint32_t w, float S) {
   return o;
 }
 
-__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 t = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(t, (u32x4*)p);
-}
-
-// One tile of kDqTileUnits units per workgroup (the partition's slices are exactly one
-// tile; a group's last slice may be shorter).
+// One step per workgroup: two waves, each writing one contiguous 2 KiB run of bf16.
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ amax,
@@ -257,33 +293,31 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Shared argument checks; fills the partition on success.  fixed_slice > 0 makes every
-// slice exactly that many units (one tile per workgroup); otherwise slices are sized so
-// that about kTargetWorkgroups workgroups cover the tensor, rounded to unit_multiple.
-int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t unit_multiple, int64_t fixed_slice,
-         Part* part, int64_t* n_groups) {
+// Shared argument checks.
+int check_shape(int64_t rows, int32_t head_dim, int64_t rpg, int64_t* n_groups) {
   if (rows < 0 || rpg <= 0) return KVFP4_EINVAL;
   if (head_dim < 64 || head_dim > 1024 || head_dim % 64 != 0) return KVFP4_EUNSUPPORTED;
-  const int64_t upr = head_dim / 8;  // units per row
   if (rows > (INT64_C(1) << 52) / head_dim) return KVFP4_EINVAL;
-  const int64_t ng = rows == 0 ? 0 : (rows - 1) / rpg + 1;
-  const int64_t rpg_eff = rpg < rows ? rpg : (rows > 0 ? rows : 1);
-  const int64_t upg = rpg_eff * upr;
-  int64_t slice;
-  if (fixed_slice > 0) {
-    slice = fixed_slice;
-  } else {
-    const int64_t want = (kTargetWorkgroups + ng - 1) / (ng > 0 ? ng : 1);
-    slice = (upg + want - 1) / want;
-    slice = (slice + unit_multiple - 1) / unit_multiple * unit_multiple;
-  }
+  *n_groups = rows == 0 ? 0 : (rows - 1) / rpg + 1;
+  return KVFP4_OK;
+}
+
+// Partition for a kernel whose workgroups each take `slice` units.  Fails (EINVAL) if the
+// grid would not fit in 32 bits.
+int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t slice, Part* part,
+         unsigned* grid) {
+  int64_t ng = 0;
+  int rc = check_shape(rows, head_dim, rpg, &ng);
+  if (rc != KVFP4_OK) return rc;
+  const int64_t upr = head_dim / 8;  // units per row (a multiple of 8)
+  const int64_t upg = (rpg < rows ? rpg : (rows > 0 ? rows : 1)) * upr;
   const int64_t spg = (upg + slice - 1) / slice;
   if (ng * spg > INT32_MAX) return KVFP4_EINVAL;
   part->units_total = rows * upr;
   part->units_per_group = upg;
   part->slice_units = slice;
   part->slices_per_group = (uint32_t)spg;
-  *n_groups = ng;
+  *grid = (unsigned)(ng * spg);
   return KVFP4_OK;
 }
 
@@ -296,6 +330,18 @@ int launched() {
   return KVFP4_OK;
 }
 
+template <int RULE, int THREADS, int UNR, int STEPS>
+int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
+                 uint8_t* codes, uint8_t* scales, const float* amax, hipStream_t s) {
+  Part part;
+  unsigned grid = 0;
+  int rc = plan(rows, head_dim, rpg, tile_units(THREADS, UNR, STEPS), &part, &grid);
+  if (rc != KVFP4_OK) return rc;
+  hipLaunchKernelGGL((quant_kernel<RULE, THREADS, UNR>), dim3(grid), dim3(THREADS), 0, s,
+                     (const uint4*)x, amax, (uint32_t*)codes, scales, part);
+  return launched();
+}
+
 }  // namespace
 }  // namespace kvfp4
 
@@ -306,52 +352,49 @@ extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
                               uint8_t* scales, float* group_amax, void* stream) {
   if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
     return KVFP4_EINVAL;
-  Part part;
-  int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, 0, &part, &ng);
+  Part apart;
+  unsigned agrid = 0;
+  int rc = plan(rows, head_dim, rows_per_group, tile_units(kAmaxThreads, kAmaxUnroll, kAmaxSteps),
+                &apart, &agrid);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!x || !codes || !scales || !group_amax) return KVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4))
     return KVFP4_EALIGN;
   hipStream_t s = (hipStream_t)stream;
-  const unsigned grid = (unsigned)(ng * part.slices_per_group);
-  const int64_t cblocks = (ng + kThreads - 1) / kThreads;
+  const int64_t ng = (rows - 1) / rows_per_group + 1;
+  const int64_t cblocks = (ng + 255) / 256;
   const unsigned cgrid = (unsigned)(cblocks < 1024 ? cblocks : 1024);
-  hipLaunchKernelGGL(clear_kernel, dim3(cgrid), dim3(kThreads), 0, s, (uint32_t*)group_amax, ng);
+  hipLaunchKernelGGL(clear_kernel, dim3(cgrid), dim3(256), 0, s, (uint32_t*)group_amax, ng);
   if ((rc = launched()) != KVFP4_OK) return rc;
-  hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kThreads), 0, s, (const uint4*)x,
-                     (uint32_t*)group_amax, part);
+  hipLaunchKernelGGL(amax_kernel, dim3(agrid), dim3(kAmaxThreads), 0, s, (const uint4*)x,
+                     (uint32_t*)group_amax, apart);
   if ((rc = launched()) != KVFP4_OK) return rc;
   switch (rule) {
     case KVFP4_RULE_STATIC6:
-      hipLaunchKernelGGL(quant_kernel<KVFP4_RULE_STATIC6>, dim3(grid), dim3(kThreads), 0, s,
-                         (const uint4*)x, (const float*)group_amax, (uint32_t*)codes, scales, part);
-      break;
+      return launch_quant<KVFP4_RULE_STATIC6, kQuantThreads, kQuantUnroll, kQuantSteps>(
+          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
     case KVFP4_RULE_STATIC4:
-      hipLaunchKernelGGL(quant_kernel<KVFP4_RULE_STATIC4>, dim3(grid), dim3(kThreads), 0, s,
-                         (const uint4*)x, (const float*)group_amax, (uint32_t*)codes, scales, part);
-      break;
+      return launch_quant<KVFP4_RULE_STATIC4, kQuantThreads, kQuantUnroll, kQuantSteps>(
+          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
     default:
-      hipLaunchKernelGGL(quant_kernel<KVFP4_RULE_MSE>, dim3(grid), dim3(kThreads), 0, s,
-                         (const uint4*)x, (const float*)group_amax, (uint32_t*)codes, scales, part);
-      break;
+      return launch_quant<KVFP4_RULE_MSE, kMseThreads, kMseUnroll, kMseSteps>(
+          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
   }
-  return launched();
 }
 
 extern "C" int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                 const float* group_amax, int64_t rows, int32_t head_dim,
                                 int64_t rows_per_group, uint16_t* y, void* stream) {
   Part part;
-  int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, kDqTileUnits, &part, &ng);
+  unsigned grid = 0;
+  int rc = plan(rows, head_dim, rows_per_group, tile_units(kDqThreads, kDqUnroll, 1), &part,
+                &grid);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!codes || !scales || !group_amax || !y) return KVFP4_EINVAL;
   if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4) || !aligned(y, 16))
     return KVFP4_EALIGN;
-  const unsigned grid = (unsigned)(ng * part.slices_per_group);
   hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, (hipStream_t)stream,
                      (const uint32_t*)codes, scales, group_amax, (uint4*)y, part);
   return launched();
@@ -360,9 +403,8 @@ extern "C" int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
 extern "C" int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
                                   int64_t* codes_bytes, int64_t* scales_bytes,
                                   int64_t* n_groups) {
-  Part part;
   int64_t ng = 0;
-  int rc = plan(rows, head_dim, rows_per_group, 64, 0, &part, &ng);
+  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (codes_bytes) *codes_bytes = rows * (head_dim / 2);
   if (scales_bytes) *scales_bytes = rows * (head_dim / 16);

@@ -167,6 +167,17 @@ def test_tiny_amax(rule):
 
 
 @pytest.mark.parametrize("rule", RULES)
+def test_tiny_blocks_and_bf16_subnormals(rule):
+    # block maxima below 2^-123 (and bf16 subnormals) in a group whose amax is 1e-19
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((128, 64), generator=g) * 1e-38
+    x[:, 32:] = torch.randn((128, 32), generator=g) * 1e-39
+    x[0, 0] = 1e-19
+    x[5, 40] = -2.0e-20
+    assert_parity(x.to(torch.bfloat16), 128, rule)
+
+
+@pytest.mark.parametrize("rule", RULES)
 def test_exact_grid_multiples(rule):
     # values that land exactly on E2M1 midpoints after scaling stress the tie rules
     g = torch.Generator().manual_seed(8)
