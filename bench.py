@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 METRIC = "KV FP4 quant+dequant GB/s (bf16+packed bytes) and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0
-DEQUANT_SOURCE = os.path.join(ROOT, "kv_cache_fp4_amd", "csrc", "kvfp4.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_fp4_amd", "csrc", f)
+                  for f in ("kvfp4.hip", "kvfp4_device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -41,6 +42,8 @@ def parse_args(argv=None):
     ap.add_argument("--rule", default=None, choices=["static_6", "static_4", "mse"],
                     help="append rule (default: mse for C3, static_6 otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attend", action="store_true",
+                    help="skip the fused dequantize+attention timing (reported beside the step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args(argv)
@@ -142,11 +145,58 @@ def cpu_baseline(cfg, rule, budget_s=12.0):
                        f"{done_dq} elements in {dt:.1f} s, single-threaded C oracle")}
 
 
+# ---- fused dequantize + attention (its own workload) ---------------------------------------
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_attend(device, steps=20, warmup=3):
+    """Q [4680, 12, 128] against the 32760-token NVFP4 K/V cache (7 groups of 4680 tokens,
+    static_6), non-causal, softmax scale 1/sqrt(128): 4*Tq*Tk*H*D flops per call."""
+    import torch
+
+    import kv_cache_fp4_amd as kv
+    import synth
+    cfg = synth.C5
+    q = synth.c5_query(device=device)
+    packed = []
+    for kv_ in (0, 1):
+        x = torch.cat([synth.chunk_group(cfg, 0, kv_, c, device=device) for c in range(cfg.chunks)])
+        packed.append(kv.kvfp4_quantize(x, cfg.rows_per_group, "static_6"))
+    (kc, ks, ka), (vc, vs, va) = packed
+    out = torch.empty_like(q)
+    scale = cfg.head_dim ** -0.5
+    call = lambda: kv.kvfp4_attend(q, kc, ks, ka, vc, vs, va, cfg.chunk_tokens, scale, out=out)  # noqa: E731
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream(device)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(device)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize(device)
+    ms = a.elapsed_time(b) / steps
+    tq, tk = synth.C5_Q_TOKENS, cfg.cache_tokens
+    flops = 4.0 * tq * tk * cfg.heads * cfg.head_dim
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": (f"{cfg.name}: non-causal attention, Q {tq}x{cfg.heads}x{cfg.head_dim} bf16 "
+                         f"over an NVFP4 K/V cache of {tk} tokens (static_6, {cfg.chunks} groups)"),
+            "ms_per_call": round(ms, 4), "flops_per_call": flops, "steps": steps,
+            "roofline": {"bound": "mfma", "kernel": "attend_kernel<128>", "achieved": round(tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
 # ---- counters ----------------------------------------------------------------------------
 
 def _source_hash():
-    with open(DEQUANT_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload_name):
@@ -253,6 +303,9 @@ def main(argv=None):
                       "append_bytes": w.append_bytes(),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
     }
+    if not args.no_attend:
+        print("bench: timing fused dequantize + attention", file=sys.stderr, flush=True)
+        res["attend"] = bench_attend(dev)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, rule)

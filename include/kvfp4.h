@@ -106,6 +106,37 @@ int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g
                      int64_t rows, int32_t head_dim, int64_t rows_per_group, uint16_t* y,
                      void* stream);
 
+/*
+ * kvfp4_attend -- attention over the packed cache, dequantizing K and V on chip.
+ * [P-KV] "CUDA De-quantization Pipeline" (K/V reconstructed to bf16 for the attention
+ * operation); [P-SF] abstract and Figure 6 (the bf16 reconstruction buffers are what keep
+ * peak memory high -- here they never exist).
+ *
+ *   O[t, h, :] = sum_j softmax_j(softmax_scale * <Q[t, h, :], K[j, h, :]>) V[j, h, :]
+ * per head h, non-causal, where K and V are the dequantized packed caches (exactly the
+ * bf16 values kvfp4_dequantize would produce).  Scores, softmax and accumulation are fp32
+ * (bf16 MFMA inputs; the softmax weights are rounded to bf16 for the second product); the
+ * output is rounded to bf16.
+ *
+ *   q                 bf16 [q_tokens, heads, head_dim]; 16-byte aligned
+ *   k_codes, v_codes  uint8 [kv_tokens, heads, head_dim/2]; 16-byte aligned
+ *   k_scales, v_scales uint8 [kv_tokens, heads, head_dim/16]; 4-byte aligned
+ *   k_amax, v_amax    float [ceil(kv_tokens / tokens_per_group)]; 4-byte aligned
+ *                     (the packed layout kvfp4_quantize writes with
+ *                      rows_per_group = tokens_per_group * heads)
+ *   kv_tokens         > 0 when q_tokens > 0
+ *   heads             1..65535
+ *   head_dim          64 or 128
+ *   softmax_scale     finite, typically 1/sqrt(head_dim)
+ *   out (out)         bf16 [q_tokens, heads, head_dim]; 16-byte aligned
+ * One kernel launch; no workspace.
+ */
+int kvfp4_attend(const uint16_t* q, int64_t q_tokens, const uint8_t* k_codes,
+                 const uint8_t* k_scales, const float* k_amax, const uint8_t* v_codes,
+                 const uint8_t* v_scales, const float* v_amax, int64_t kv_tokens, int32_t heads,
+                 int32_t head_dim, int64_t tokens_per_group, float softmax_scale, uint16_t* out,
+                 void* stream);
+
 /* Host-side size helper: bytes of codes and scales and the number of group amax floats
  * for a tensor of `rows` rows.  Returns KVFP4_EINVAL / KVFP4_EUNSUPPORTED like the calls
  * above.  Any output pointer may be NULL. */

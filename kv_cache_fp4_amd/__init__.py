@@ -35,6 +35,8 @@ def _load() -> ctypes.CDLL:
     L.kvfp4_quantize.restype = ctypes.c_int
     L.kvfp4_dequantize.argtypes = [P, P, P, i64, i32, i64, P, P]
     L.kvfp4_dequantize.restype = ctypes.c_int
+    L.kvfp4_attend.argtypes = [P, i64, P, P, P, P, P, P, i64, i32, i32, i64, ctypes.c_float, P, P]
+    L.kvfp4_attend.restype = ctypes.c_int
     L.kvfp4_packed_sizes.argtypes = [i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
     L.kvfp4_packed_sizes.restype = ctypes.c_int
@@ -125,5 +127,26 @@ def kvfp4_dequantize(codes, scales, group_amax, rows_per_group: int, y=None, str
     return y
 
 
-__all__ = ["kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
+def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
+                 tokens_per_group: int, softmax_scale=None, out=None, stream=None):
+    """Attention of bf16 ``q`` [q_tokens, heads, head_dim] over a packed K/V cache
+    (codes [kv_tokens*heads, head_dim/2], scales [kv_tokens*heads, head_dim/16], one amax per
+    ``tokens_per_group`` tokens), dequantized on chip.  Returns bf16 [q_tokens, heads, head_dim]."""
+    import math
+
+    import torch
+    q_tokens, heads, head_dim = q.shape
+    kv_tokens = k_codes.numel() * 2 // (heads * head_dim) if heads * head_dim else 0
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    if out is None:
+        out = torch.empty((q_tokens, heads, head_dim), dtype=torch.bfloat16, device=q.device)
+    _check(lib.kvfp4_attend(_ptr(q), q_tokens, _ptr(k_codes), _ptr(k_scales), _ptr(k_amax),
+                            _ptr(v_codes), _ptr(v_scales), _ptr(v_amax), kv_tokens, heads,
+                            head_dim, tokens_per_group, float(softmax_scale), _ptr(out),
+                            _stream(stream, q.device)))
+    return out
+
+
+__all__ = ["kvfp4_attend", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
            "lib", "LIB_PATH"]

@@ -16,7 +16,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "kvfp4.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("kvfp4.hip", "kvfp4_attend.hip")]
 LIB = os.path.join(PKG, "libkvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -28,18 +28,20 @@ HIP_FLAGS = [
 ]
 
 
-def compile_hip(src: str, out: str, extra_includes=()) -> str:
+def compile_hip(srcs, out: str, extra_includes=()) -> str:
+    if isinstance(srcs, str):
+        srcs = [srcs]
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     for d in extra_includes:
         inc += ["-I", d]
-    cmd = [HIPCC, *HIP_FLAGS, *inc, "-o", out + ".tmp", src]
+    cmd = [HIPCC, *HIP_FLAGS, *inc, "-o", out + ".tmp", *srcs]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
 
 
 def build() -> str:
-    return compile_hip(SRC, LIB)
+    return compile_hip(SRCS, LIB)
 
 
 if __name__ == "__main__":

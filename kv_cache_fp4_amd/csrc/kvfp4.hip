@@ -252,17 +252,6 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict_
 
 // ---- dequantize ([P-NVFP4] "Stage 3"; [P-KV] "CUDA De-quantization Pipeline") -----------
 
-__device__ __forceinline__ uint4 decode8(uint32_t w, float S) {
-  const f32x2 a = e2m1_decode2<0>(w), b = e2m1_decode2<1>(w);
-  const f32x2 c = e2m1_decode2<2>(w), d = e2m1_decode2<3>(w);
-  uint4 o;
-  o.x = pack_bf16x2(a.x * S, a.y * S);
-  o.y = pack_bf16x2(b.x * S, b.y * S);
-  o.z = pack_bf16x2(c.x * S, c.y * S);
-  o.w = pack_bf16x2(d.x * S, d.y * S);
-  return o;
-}
-
 // One step per workgroup: two waves, each writing one contiguous 2 KiB run of bf16.
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
@@ -343,6 +332,13 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
 }
 
 }  // namespace
+
+// Records a failed launch for kvfp4_last_hip_error() (shared with kvfp4_attend.hip).
+int set_last_hip_error(int e) {
+  g_last_hip_error = e;
+  return KVFP4_EHIP;
+}
+
 }  // namespace kvfp4
 
 using namespace kvfp4;

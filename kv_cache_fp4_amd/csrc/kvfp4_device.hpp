@@ -96,4 +96,17 @@ __device__ __forceinline__ f32x2 e2m1_decode2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
+// Dequantize one code dword (8 elements) with block scale S (= E4M3(sf) * A/2688): each
+// E2M1 value times S in binary32, rounded to bf16.  Output element i in bf16 lane i.
+__device__ __forceinline__ uint4 decode8(uint32_t w, float S) {
+  const f32x2 a = e2m1_decode2<0>(w), b = e2m1_decode2<1>(w);
+  const f32x2 c = e2m1_decode2<2>(w), d = e2m1_decode2<3>(w);
+  uint4 o;
+  o.x = pack_bf16x2(a.x * S, a.y * S);
+  o.y = pack_bf16x2(b.x * S, b.y * S);
+  o.z = pack_bf16x2(c.x * S, c.y * S);
+  o.w = pack_bf16x2(d.x * S, d.y * S);
+  return o;
+}
+
 }  // namespace kvfp4

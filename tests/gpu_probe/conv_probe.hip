@@ -76,3 +76,29 @@ extern "C" int probe_bf16_pack(const float* f, int64_t n2, uint32_t* out, void* 
   hipLaunchKernelGGL(bf16_pack_k, dim3(blocks(n2)), dim3(kT), 0, (hipStream_t)s, f, n2, out);
   return status();
 }
+
+// One 32x32x16 bf16 MFMA on one wave with the operand/result lane layout the attention
+// kernel assumes: A[32x16] lane l holds row l%32, k = 8*(l/32)+i; B[16x32] lane l holds
+// column l%32, k = 8*(l/32)+i; D[32x32] register j of lane l is row 8*(j/4)+4*(l/32)+j%4,
+// column l%32.  a: row-major fp32 [32][16], b: row-major [16][32], d: row-major [32][32].
+namespace {
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__global__ void mfma_layout_k(const float* __restrict__ a, const float* __restrict__ b,
+                              float* __restrict__ d) {
+  const int l = threadIdx.x;  // launched with exactly 64 threads
+  const int col = l & 31, hi = l >> 5;
+  bf16x8_t av, bv;
+  for (int i = 0; i < 8; ++i) {
+    av[i] = (__bf16)a[col * 16 + 8 * hi + i];   // row = l%32
+    bv[i] = (__bf16)b[(8 * hi + i) * 32 + col]; // column = l%32
+  }
+  f32x16_t acc = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  for (int j = 0; j < 16; ++j) d[(8 * (j / 4) + 4 * hi + (j % 4)) * 32 + col] = acc[j];
+}
+}  // namespace
+extern "C" int probe_mfma_32x32x16_bf16(const float* a, const float* b, float* d, void* s) {
+  hipLaunchKernelGGL(mfma_layout_k, dim3(1), dim3(64), 0, (hipStream_t)s, a, b, d);
+  return status();
+}

@@ -99,3 +99,34 @@ def test_packed_sizes():
     assert kv.kvfp4_packed_sizes(0, 64, 10) == (0, 0, 0)
     with pytest.raises(kv.KVFP4Error):
         kv.kvfp4_packed_sizes(10, 80, 10)
+
+
+def at(q=A16, tq=10, kc=A16, ks=A16, ka=A16, vc=A16, vs=A16, va=A16, tk=10, h=2, d=128, tpg=5,
+       scale=0.1, out=A16):
+    return lib.kvfp4_attend(q, tq, kc, ks, ka, vc, vs, va, tk, h, d, tpg, scale, out, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(tq=-1), KVFP4_EINVAL),
+    (dict(tk=0), KVFP4_EINVAL),
+    (dict(h=0), KVFP4_EINVAL),
+    (dict(tpg=0), KVFP4_EINVAL),
+    (dict(scale=float("inf")), KVFP4_EINVAL),
+    (dict(scale=float("nan")), KVFP4_EINVAL),
+    (dict(d=256), KVFP4_EUNSUPPORTED),
+    (dict(d=96), KVFP4_EUNSUPPORTED),
+    (dict(q=None), KVFP4_EINVAL),
+    (dict(va=None), KVFP4_EINVAL),
+    (dict(out=None), KVFP4_EINVAL),
+    (dict(q=A16 + 8), KVFP4_EALIGN),
+    (dict(kc=A16 + 4), KVFP4_EALIGN),
+    (dict(vs=A16 + 2), KVFP4_EALIGN),
+    (dict(out=A16 + 2), KVFP4_EALIGN),
+    (dict(h=70000), KVFP4_EINVAL),
+])
+def test_attend_rejects(kw, want):
+    assert at(**kw) == want
+
+
+def test_attend_zero_queries_is_a_noop():
+    assert at(tq=0, q=None, kc=None, ks=None, ka=None, vc=None, vs=None, va=None, out=None) == KVFP4_OK

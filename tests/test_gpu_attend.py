@@ -1,0 +1,115 @@
+"""GPU parity for the fused dequantize + attention kernel against the oracle.
+
+The oracle quantizes K and V itself from the same bf16 inputs, dequantizes them, and
+evaluates softmax(scale * Q K^T) V per head in double precision; the GPU quantizes with
+kvfp4_quantize and attends with kvfp4_attend.  Tolerance (fp32 softmax, bf16 MFMA
+operands, bf16 weights and output): max |gpu - oracle| <= 2e-2 and
+||gpu - oracle||_2 <= 1e-2 ||oracle||_2.  A "peaky" variant (query scale 4, logit standard
+deviation about 4) makes a few keys dominate, so the outputs are O(1) rather than near 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _f(h):
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def run_case(tq, tk, H, D, tpg, q_scale, seed, rule="static_6", rows=None):
+    import kv_cache_fp4_amd as kv
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((tq, H, D), generator=g) * q_scale).to(torch.bfloat16)
+    k = torch.randn((tk, H, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((tk, H, D), generator=g).to(torch.bfloat16)
+    rpg = tpg * H
+    kc, ks, ka = kv.kvfp4_quantize(k.to(DEV), rpg, rule)
+    vc, vs, va = kv.kvfp4_quantize(v.to(DEV), rpg, rule)
+    scale = 1.0 / math.sqrt(D)
+    o = kv.kvfp4_attend(q.to(DEV), kc, ks, ka, vc, vs, va, tpg, scale)
+    torch.cuda.synchronize()
+    # oracle: its own quantize + dequantize of the same inputs, then attention in double
+    kd = oracle.dequantize(*oracle.quantize(_u16(k).reshape(-1, D), rpg, rule), rpg).reshape(tk, H, D)
+    vd = oracle.dequantize(*oracle.quantize(_u16(v).reshape(-1, D), rpg, rule), rpg).reshape(tk, H, D)
+    if rows is None:
+        rows = np.arange(tq * H, dtype=np.int64)
+    ref = _f(oracle.attend_rows(_u16(q), kd, vd, scale, rows)).astype(np.float64)
+    got = _f(_u16(o).reshape(-1, D)[rows]).astype(np.float64)
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    return err.max(), rel, np.abs(ref).max()
+
+
+@pytest.mark.parametrize("tq,tk,H,D,tpg", [
+    (128, 64, 1, 128, 64),       # one tile each way
+    (300, 1000, 3, 128, 333),    # ragged query and key tails, group boundaries inside steps
+    (77, 257, 2, 64, 100),       # head_dim 64
+    (200, 130, 2, 128, 10),      # groups shorter than a key step
+])
+@pytest.mark.parametrize("q_scale", [128 ** -0.5, 4.0])
+def test_attend_matches_oracle(tq, tk, H, D, tpg, q_scale):
+    mx, rel, ref_max = run_case(tq, tk, H, D, tpg, q_scale, seed=tq + tk + D)
+    assert mx <= 2e-2 and rel <= 1e-2, (mx, rel, ref_max)
+
+
+def test_single_key_returns_its_value_row():
+    import kv_cache_fp4_amd as kv
+    g = torch.Generator().manual_seed(3)
+    H, D = 4, 128
+    q = torch.randn((50, H, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, H, D), generator=g).to(torch.bfloat16)
+    kc, ks, ka = kv.kvfp4_quantize(v.to(DEV), H, "mse")
+    vc, vs, va = kv.kvfp4_quantize(v.to(DEV), H, "mse")
+    o = kv.kvfp4_attend(q.to(DEV), kc, ks, ka, vc, vs, va, 1)
+    vd = kv.kvfp4_dequantize(vc, vs, va, H).view(1, H, D)
+    torch.cuda.synchronize()
+    # equal as values: 1 * (-0) accumulated onto +0 gives +0, which compares equal to -0
+    assert torch.equal(o.float(), vd.expand(50, H, D).float())
+
+
+def test_full_size_sampled_rows():
+    """Q [4680, 12, 128] against a 32760-token cache (7 groups of 4680 tokens), static_6;
+    the oracle recomputes 32 sampled query rows of every head."""
+    import kv_cache_fp4_amd as kv
+    cfg = synth.C5
+    tk, H, D = cfg.cache_tokens, cfg.heads, cfg.head_dim
+    q = synth.c5_query()
+    k = torch.cat([synth.chunk_group(cfg, 0, 0, c) for c in range(cfg.chunks)])
+    v = torch.cat([synth.chunk_group(cfg, 0, 1, c) for c in range(cfg.chunks)])
+    rpg = cfg.rows_per_group
+    kc, ks, ka = kv.kvfp4_quantize(k.to(DEV), rpg, "static_6")
+    vc, vs, va = kv.kvfp4_quantize(v.to(DEV), rpg, "static_6")
+    o = kv.kvfp4_attend(q.to(DEV), kc, ks, ka, vc, vs, va, cfg.chunk_tokens, D ** -0.5)
+    torch.cuda.synchronize()
+    kd = oracle.dequantize(*oracle.quantize(_u16(k).reshape(-1, D), rpg, "static_6"), rpg).reshape(tk, H, D)
+    vd = oracle.dequantize(*oracle.quantize(_u16(v).reshape(-1, D), rpg, "static_6"), rpg).reshape(tk, H, D)
+    rng = np.random.default_rng(5)
+    toks = np.concatenate([[0, synth.C5_Q_TOKENS - 1], rng.integers(0, synth.C5_Q_TOKENS, 30)])
+    rows = (toks[:, None] * H + np.arange(H)[None, :]).reshape(-1).astype(np.int64)
+    ref = _f(oracle.attend_rows(_u16(q), kd, vd, D ** -0.5, rows)).astype(np.float64)
+    got = _f(_u16(o).reshape(-1, D)[rows]).astype(np.float64)
+    mx = np.abs(got - ref).max()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert mx <= 2e-2 and rel <= 1e-2, (mx, rel)
+
+
+def test_attend_rejects_bad_arguments():
+    import kv_cache_fp4_amd as kv
+    q = torch.zeros((4, 2, 96), dtype=torch.bfloat16, device=DEV)
+    c = torch.zeros((8, 48), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((8, 6), dtype=torch.uint8, device=DEV)
+    a = torch.zeros((1,), dtype=torch.float32, device=DEV)
+    with pytest.raises(kv.KVFP4Error):
+        kv.kvfp4_attend(q, c, s, a, c, s, a, 4)

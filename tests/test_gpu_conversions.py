@@ -109,3 +109,20 @@ def test_bf16_pack_matches_oracle(probe):
     want = oracle.float_to_bf16(f)
     bad = np.nonzero(halves != want)[0]
     assert bad.size == 0, [(float(f[i]), hex(halves[i]), hex(want[i])) for i in bad[:10]]
+
+
+def test_mfma_32x32x16_bf16_lane_layout(probe):
+    """The operand and accumulator lane layout the attention kernel is written against."""
+    probe.probe_mfma_32x32x16_bf16.argtypes = [ctypes.c_void_p] * 4
+    probe.probe_mfma_32x32x16_bf16.restype = ctypes.c_int
+    rng = np.random.default_rng(34)
+    # small integers are exact in bf16 and their products/sums exact in fp32
+    a = rng.integers(-4, 5, (32, 16)).astype(np.float32)
+    b = rng.integers(-4, 5, (16, 32)).astype(np.float32)
+    dev = torch.device("cuda:0")
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    td = torch.zeros((32, 32), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    assert probe.probe_mfma_32x32x16_bf16(ta.data_ptr(), tb.data_ptr(), td.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(td.cpu().numpy(), a @ b)
