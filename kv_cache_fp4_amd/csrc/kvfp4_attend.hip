@@ -56,8 +56,49 @@ struct AttShape {
 // Position of key r (0..15) inside its 16-key block of the V^T tile: bits 2 and 3 swapped.
 __device__ __forceinline__ int vperm(int r) { return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Raw (still packed) K/V data of one 64-key step held by one thread: 4 K units
+// (key = u / UPR, d-chunk = u % UPR for u = tid + 256 r) and, for V, four consecutive keys
+// of one d-chunk.
 template <int D>
-__global__ __launch_bounds__(kAtThreads) void attend_kernel(
+struct Raw {
+  static constexpr int KU = (kAtBN * (D / 8) + kAtThreads - 1) / kAtThreads;  // K units
+  uint32_t kc[KU], ks[KU];
+  uint32_t vc[4], vs[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_raw(Raw<D>& r, int64_t t0, int64_t Tk, int H, int head,
+                                         const uint32_t* __restrict__ kcodes,
+                                         const uint8_t* __restrict__ kscales,
+                                         const uint32_t* __restrict__ vcodes,
+                                         const uint8_t* __restrict__ vscales) {
+  using S = AttShape<D>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int r_ = 0; r_ < Raw<D>::KU; ++r_) {
+    const int ui = tid + kAtThreads * r_;
+    const int key = ui / S::UPR, j = ui % S::UPR;
+    const int64_t t = t0 + key;
+    const bool ok = ui < kAtBN * S::UPR && t < Tk;
+    const int64_t row = t * H + head;
+    r.kc[r_] = ok ? kcodes[row * S::UPR + j] : 0u;
+    r.ks[r_] = ok ? (uint32_t)kscales[row * (D / 16) + (j >> 1)] : 0u;
+  }
+  const int vi = tid;
+  const bool vjob = vi < (kAtBN / 4) * S::UPR;
+  const int j = vi / (kAtBN / 4), kq = vi % (kAtBN / 4);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int64_t t = t0 + 4 * kq + kk;
+    const bool ok = vjob && t < Tk;
+    const int64_t row = t * H + head;
+    r.vc[kk] = ok ? vcodes[row * S::UPR + j] : 0u;
+    r.vs[kk] = ok ? (uint32_t)vscales[row * (D / 16) + (j >> 1)] : 0u;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAtThreads, 2) void attend_kernel(
     const uint16_t* __restrict__ q, int64_t Tq, const uint32_t* __restrict__ kcodes,
     const uint8_t* __restrict__ kscales, const float* __restrict__ kamax,
     const uint32_t* __restrict__ vcodes, const uint8_t* __restrict__ vscales,
@@ -88,7 +129,13 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(
   f32x16 o[S::DB];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) o[db] = f32x16{};
+  // Running max (base-2 logits) and running sum.  The max is only moved when a new score
+  // exceeds it by more than 8, so most steps skip the rescale of O; weights stay <= 2^8.
   float m_run = -INFINITY, l_run = 0.0f;
+  const bool short_groups = tpg < kAtBN;
+
+  Raw<D> raw;
+  load_raw<D>(raw, 0, Tk, H, head, kcodes, kscales, vcodes, vscales);
 
   for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN) {
     // Group decode scales of this step's keys: a step crosses at most one group boundary
@@ -99,37 +146,31 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(
     const float kd0 = kamax[g0] / kGlobalDiv, vd0 = vamax[g0] / kGlobalDiv;
     const float kd1 = two ? kamax[g0 + 1] / kGlobalDiv : kd0;
     const float vd1 = two ? vamax[g0 + 1] / kGlobalDiv : vd0;
-    const bool short_groups = tpg < kAtBN;
 
     __syncthreads();  // the previous step's LDS reads are done
     // K tile -> LDS, row-major [key][d]: 16 B per unit.
-    for (int ui = tid; ui < kAtBN * S::UPR; ui += kAtThreads) {
-      const int key = ui / S::UPR, j = ui % S::UPR;
-      const int64_t t = t0 + key;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (t < Tk) {
-        const int64_t row = t * H + head;
-        const float sd = short_groups ? kamax[t / tpg] / kGlobalDiv : (t < bnd ? kd0 : kd1);
-        val = decode8(kcodes[row * S::UPR + j],
-                      e4m3_decode(kscales[row * (D / 16) + (j >> 1)]) * sd);
+#pragma unroll
+    for (int r_ = 0; r_ < Raw<D>::KU; ++r_) {
+      const int ui = tid + kAtThreads * r_;
+      if (ui < kAtBN * S::UPR) {
+        const int key = ui / S::UPR, j = ui % S::UPR;
+        const int64_t t = t0 + key;
+        const float sd = short_groups ? (t < Tk ? kamax[t / tpg] / kGlobalDiv : 0.0f)
+                                      : (t < bnd ? kd0 : kd1);
+        *(uint4*)(k_lds + key * S::KSTR + j * 8) = decode8(raw.kc[r_], e4m3_decode(raw.ks[r_]) * sd);
       }
-      *(uint4*)(k_lds + key * S::KSTR + j * 8) = val;
     }
     // V tile -> LDS transposed [d][key'], four consecutive keys per thread so that each
     // d row gets one 8-byte write; key' = vperm order inside 16-key blocks.
-    for (int vi = tid; vi < (kAtBN / 4) * S::UPR; vi += kAtThreads) {
-      const int j = vi / (kAtBN / 4), kq = vi % (kAtBN / 4);
+    if (tid < (kAtBN / 4) * S::UPR) {
+      const int j = tid / (kAtBN / 4), kq = tid % (kAtBN / 4);
       uint4 w[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int64_t t = t0 + 4 * kq + kk;
-        w[kk] = make_uint4(0, 0, 0, 0);
-        if (t < Tk) {
-          const int64_t row = t * H + head;
-          const float sd = short_groups ? vamax[t / tpg] / kGlobalDiv : (t < bnd ? vd0 : vd1);
-          w[kk] = decode8(vcodes[row * S::UPR + j],
-                          e4m3_decode(vscales[row * (D / 16) + (j >> 1)]) * sd);
-        }
+        const float sd = short_groups ? (t < Tk ? vamax[t / tpg] / kGlobalDiv : 0.0f)
+                                      : (t < bnd ? vd0 : vd1);
+        w[kk] = decode8(raw.vc[kk], e4m3_decode(raw.vs[kk]) * sd);
       }
       const int pos = (4 * kq & ~15) | vperm((4 * kq) & 15);
 #pragma unroll
@@ -143,6 +184,8 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(
       }
     }
     __syncthreads();
+    // Fetch the next step's packed K/V now; the loads complete while this step computes.
+    if (t0 + kAtBN < Tk) load_raw<D>(raw, t0 + kAtBN, Tk, H, head, kcodes, kscales, vcodes, vscales);
 
     // S^T = K Q^T for 64 keys (two 32-key row blocks) x the wave's 32 queries.
     f32x16 s[2];
@@ -155,33 +198,47 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kc], s[rb], 0, 0, 0);
       }
     }
-    // Online softmax for query l32 (base-2 exponent); keys past Tk are masked.
+    // Online softmax for query l32 (base-2 exponent).  Keys past Tk (last step only) are
+    // masked to -inf.
     float mx = -INFINITY;
+    if (t0 + kAtBN <= Tk) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t key = t0 + 32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3);
-        const float v = key < Tk ? s[rb][j] * qk_scale_log2 : -INFINITY;
-        s[rb][j] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int j = 0; j < 16; ++j) {
+          s[rb][j] *= qk_scale_log2;
+          mx = fmaxf(mx, s[rb][j]);
+        }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = 32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3);
+          s[rb][j] = (t0 + key < Tk) ? s[rb][j] * qk_scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[rb][j]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: key t0 < Tk is in this step
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // Move the running max (and rescale O and l) only when some query of the wave needs it.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);  // finite: key t0 < Tk is in this step
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) o[db] *= alpha;
+    }
     float ps = 0.0f;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(s[rb][j] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[rb][j] - m_run);
         s[rb][j] = p;
         ps += p;
       }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) o[db] *= alpha;
+    l_run += ps;
 
     // O^T += V^T P^T, 16 keys per MFMA.
 #pragma unroll
