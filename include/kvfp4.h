@@ -127,7 +127,7 @@ int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g
  *   kv_tokens         > 0 when q_tokens > 0
  *   heads             1..65535
  *   head_dim          64 or 128
- *   softmax_scale     finite, typically 1/sqrt(head_dim)
+ *   softmax_scale     finite and > 0, typically 1/sqrt(head_dim)
  *   out (out)         bf16 [q_tokens, heads, head_dim]; 16-byte aligned
  * One kernel launch; no workspace.
  */

@@ -18,7 +18,7 @@
 // Mapping (v_mfma_f32_32x32x16_bf16; a lane holds 8 consecutive k of one row of A and of
 // one column of B; accumulator register j of lane l is row 8*(j/4) + 4*(l/32) + j%4,
 // column l%32):
-//   - a workgroup is 4 waves x 32 queries of one head; a step covers 64 keys;
+//   - a workgroup is 8 waves x 32 queries of one head; a step covers 64 keys;
 //   - S^T = K Q^T: A = K rows from LDS, B = the wave's Q^T held in registers, so each lane
 //     ends up owning one query (column) and 32 of the 64 keys of the step; the other 32
 //     keys of that query sit in lane l ^ 32, one exchange gives the row max / row sum;
@@ -39,10 +39,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kAtThreads = 256;  // 4 waves
-constexpr int kAtWaveQ = 32;     // queries per wave
-constexpr int kAtBM = 128;       // queries per workgroup
-constexpr int kAtBN = 64;        // keys per step
+constexpr int kAtWaves = 8;                  // waves per workgroup (2 per SIMD)
+constexpr int kAtThreads = 64 * kAtWaves;
+constexpr int kAtWaveQ = 32;                 // queries per wave
+constexpr int kAtBM = kAtWaveQ * kAtWaves;   // queries per workgroup
+constexpr int kAtBN = 64;                    // keys per step
 
 template <int D>
 struct AttShape {
@@ -56,14 +57,16 @@ struct AttShape {
 // Position of key r (0..15) inside its 16-key block of the V^T tile: bits 2 and 3 swapped.
 __device__ __forceinline__ int vperm(int r) { return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Raw (still packed) K/V data of one 64-key step held by one thread: 4 K units
-// (key = u / UPR, d-chunk = u % UPR for u = tid + 256 r) and, for V, four consecutive keys
-// of one d-chunk.
+// Raw (still packed) K/V data of one 64-key step held by one thread: KU units of K
+// (key = u / UPR, d-chunk = u % UPR for u = tid + kAtThreads * r) and VU pairs of
+// consecutive V keys of one d-chunk (pair p = tid + kAtThreads * r: d-chunk p / 32, keys
+// 2 (p % 32) and 2 (p % 32) + 1).
 template <int D>
 struct Raw {
-  static constexpr int KU = (kAtBN * (D / 8) + kAtThreads - 1) / kAtThreads;  // K units
+  static constexpr int KU = (kAtBN * (D / 8) + kAtThreads - 1) / kAtThreads;
+  static constexpr int VU = ((kAtBN / 2) * (D / 8) + kAtThreads - 1) / kAtThreads;
   uint32_t kc[KU], ks[KU];
-  uint32_t vc[4], vs[4];
+  uint32_t vc[VU][2], vs[VU][2];
 };
 
 template <int D>
@@ -84,21 +87,23 @@ __device__ __forceinline__ void load_raw(Raw<D>& r, int64_t t0, int64_t Tk, int 
     r.kc[r_] = ok ? kcodes[row * S::UPR + j] : 0u;
     r.ks[r_] = ok ? (uint32_t)kscales[row * (D / 16) + (j >> 1)] : 0u;
   }
-  const int vi = tid;
-  const bool vjob = vi < (kAtBN / 4) * S::UPR;
-  const int j = vi / (kAtBN / 4), kq = vi % (kAtBN / 4);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int64_t t = t0 + 4 * kq + kk;
-    const bool ok = vjob && t < Tk;
-    const int64_t row = t * H + head;
-    r.vc[kk] = ok ? vcodes[row * S::UPR + j] : 0u;
-    r.vs[kk] = ok ? (uint32_t)vscales[row * (D / 16) + (j >> 1)] : 0u;
+  for (int r_ = 0; r_ < Raw<D>::VU; ++r_) {
+    const int pi = tid + kAtThreads * r_;
+    const int j = pi / (kAtBN / 2), kp = pi % (kAtBN / 2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int64_t t = t0 + 2 * kp + kk;
+      const bool ok = pi < (kAtBN / 2) * S::UPR && t < Tk;
+      const int64_t row = t * H + head;
+      r.vc[r_][kk] = ok ? vcodes[row * S::UPR + j] : 0u;
+      r.vs[r_][kk] = ok ? (uint32_t)vscales[row * (D / 16) + (j >> 1)] : 0u;
+    }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kAtThreads, 2) void attend_kernel(
+__global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     const uint16_t* __restrict__ q, int64_t Tq, const uint32_t* __restrict__ kcodes,
     const uint8_t* __restrict__ kscales, const float* __restrict__ kamax,
     const uint32_t* __restrict__ vcodes, const uint8_t* __restrict__ vscales,
@@ -160,27 +165,31 @@ __global__ __launch_bounds__(kAtThreads, 2) void attend_kernel(
         *(uint4*)(k_lds + key * S::KSTR + j * 8) = decode8(raw.kc[r_], e4m3_decode(raw.ks[r_]) * sd);
       }
     }
-    // V tile -> LDS transposed [d][key'], four consecutive keys per thread so that each
-    // d row gets one 8-byte write; key' = vperm order inside 16-key blocks.
-    if (tid < (kAtBN / 4) * S::UPR) {
-      const int j = tid / (kAtBN / 4), kq = tid % (kAtBN / 4);
-      uint4 w[4];
+    // V tile -> LDS transposed [d][key'], two consecutive keys per thread so that each d
+    // row gets one 4-byte write; key' = vperm order inside 16-key blocks (keeps pairs).
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int64_t t = t0 + 4 * kq + kk;
-        const float sd = short_groups ? (t < Tk ? vamax[t / tpg] / kGlobalDiv : 0.0f)
-                                      : (t < bnd ? vd0 : vd1);
-        w[kk] = decode8(raw.vc[kk], e4m3_decode(raw.vs[kk]) * sd);
-      }
-      const int pos = (4 * kq & ~15) | vperm((4 * kq) & 15);
+    for (int r_ = 0; r_ < Raw<D>::VU; ++r_) {
+      const int pi = tid + kAtThreads * r_;
+      if (pi < (kAtBN / 2) * S::UPR) {
+        const int j = pi / (kAtBN / 2), kp = pi % (kAtBN / 2);
+        uint4 w[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sh = (i & 1) * 16;
-        const uint32_t e0 = ((&w[0].x)[i >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e1 = ((&w[1].x)[i >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e2 = ((&w[2].x)[i >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e3 = ((&w[3].x)[i >> 1] >> sh) & 0xFFFFu;
-        *(uint2*)(v_lds + (8 * j + i) * S::VSTR + pos) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        for (int kk = 0; kk < 2; ++kk) {
+          const int64_t t = t0 + 2 * kp + kk;
+          const float sd = short_groups ? (t < Tk ? vamax[t / tpg] / kGlobalDiv : 0.0f)
+                                        : (t < bnd ? vd0 : vd1);
+          w[kk] = decode8(raw.vc[r_][kk], e4m3_decode(raw.vs[r_][kk]) * sd);
+        }
+        const int pos = (2 * kp & ~15) | vperm((2 * kp) & 15);
+        const uint32_t* w0 = &w[0].x;
+        const uint32_t* w1 = &w[1].x;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {  // d = 8 j + 2 i2 and 8 j + 2 i2 + 1
+          *(uint32_t*)(v_lds + (8 * j + 2 * i2) * S::VSTR + pos) =
+              (w0[i2] & 0xFFFFu) | (w1[i2] << 16);
+          *(uint32_t*)(v_lds + (8 * j + 2 * i2 + 1) * S::VSTR + pos) =
+              (w0[i2] >> 16) | (w1[i2] & 0xFFFF0000u);
+        }
       }
     }
     __syncthreads();
@@ -198,28 +207,24 @@ __global__ __launch_bounds__(kAtThreads, 2) void attend_kernel(
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kc], s[rb], 0, 0, 0);
       }
     }
-    // Online softmax for query l32 (base-2 exponent).  Keys past Tk (last step only) are
-    // masked to -inf.
+    // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
+    // > 0, so the max is taken on the raw scores and scaled once.  Keys past Tk (last step
+    // only) are masked to -inf.
     float mx = -INFINITY;
-    if (t0 + kAtBN <= Tk) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          s[rb][j] *= qk_scale_log2;
-          mx = fmaxf(mx, s[rb][j]);
-        }
-    } else {
+    if (t0 + kAtBN > Tk) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = 32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3);
-          s[rb][j] = (t0 + key < Tk) ? s[rb][j] * qk_scale_log2 : -INFINITY;
-          mx = fmaxf(mx, s[rb][j]);
+          if (t0 + key >= Tk) s[rb][j] = -INFINITY;
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[rb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * qk_scale_log2;
     // Move the running max (and rescale O and l) only when some query of the wave needs it.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
       const float m_new = fmaxf(m_run, mx);  // finite: key t0 < Tk is in this step
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attend_kernel(
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(s[rb][j] - m_run);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][j], qk_scale_log2, -m_run));
         s[rb][j] = p;
         ps += p;
       }
@@ -288,7 +293,7 @@ extern "C" int kvfp4_attend(const uint16_t* q, int64_t q_tokens, const uint8_t* 
                             float softmax_scale, uint16_t* out, void* stream) {
   using namespace kvfp4;
   if (q_tokens < 0 || kv_tokens < 0 || heads <= 0 || tokens_per_group <= 0 ||
-      !isfinite(softmax_scale))
+      !isfinite(softmax_scale) || !(softmax_scale > 0.0f))
     return KVFP4_EINVAL;
   if (head_dim != 64 && head_dim != 128) return KVFP4_EUNSUPPORTED;
   if (heads > 65535 || (q_tokens + kAtBM - 1) / kAtBM > INT32_MAX ||

@@ -113,6 +113,8 @@ def at(q=A16, tq=10, kc=A16, ks=A16, ka=A16, vc=A16, vs=A16, va=A16, tk=10, h=2,
     (dict(tpg=0), KVFP4_EINVAL),
     (dict(scale=float("inf")), KVFP4_EINVAL),
     (dict(scale=float("nan")), KVFP4_EINVAL),
+    (dict(scale=0.0), KVFP4_EINVAL),
+    (dict(scale=-0.5), KVFP4_EINVAL),
     (dict(d=256), KVFP4_EUNSUPPORTED),
     (dict(d=96), KVFP4_EUNSUPPORTED),
     (dict(q=None), KVFP4_EINVAL),
