@@ -57,52 +57,176 @@ struct AttShape {
 // Position of key r (0..15) inside its 16-key block of the V^T tile: bits 2 and 3 swapped.
 __device__ __forceinline__ int vperm(int r) { return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Raw (still packed) K/V data of one 64-key step held by one thread: KU units of K
-// (key = u / UPR, d-chunk = u % UPR for u = tid + kAtThreads * r) and VU pairs of
-// consecutive V keys of one d-chunk (pair p = tid + kAtThreads * r: d-chunk p / 32, keys
-// 2 (p % 32) and 2 (p % 32) + 1).
+// Per-thread share of one 64-key step.  K: KU units (u = tid + kAtThreads r: key u / UPR,
+// d-chunk u % UPR).  V: VU pairs of consecutive keys of one d-chunk (p = tid + kAtThreads r:
+// d-chunk p / 32, keys 2 (p % 32) and 2 (p % 32) + 1).  Offsets are relative to the step's
+// first key and are the same for every step.
 template <int D>
-struct Raw {
-  static constexpr int KU = (kAtBN * (D / 8) + kAtThreads - 1) / kAtThreads;
-  static constexpr int VU = ((kAtBN / 2) * (D / 8) + kAtThreads - 1) / kAtThreads;
-  uint32_t kc[KU], ks[KU];
-  uint32_t vc[VU][2], vs[VU][2];
+struct Share {
+  static constexpr int UPR = D / 8;
+  static constexpr int KU = (kAtBN * UPR + kAtThreads - 1) / kAtThreads;
+  static constexpr int VU = ((kAtBN / 2) * UPR + kAtThreads - 1) / kAtThreads;
+  int kkey[KU];            // key index in the step (>= kAtBN: no unit)
+  uint32_t koff[KU];       // code dword offset
+  uint32_t ksoff[KU];      // scale byte offset
+  int vkey[VU];            // first key of the pair (>= kAtBN: no pair)
+  int vj[VU];              // d-chunk
+  uint32_t voff[VU][2];
+  uint32_t vsoff[VU][2];
 };
 
 template <int D>
-__device__ __forceinline__ void load_raw(Raw<D>& r, int64_t t0, int64_t Tk, int H, int head,
-                                         const uint32_t* __restrict__ kcodes,
-                                         const uint8_t* __restrict__ kscales,
-                                         const uint32_t* __restrict__ vcodes,
-                                         const uint8_t* __restrict__ vscales) {
-  using S = AttShape<D>;
+__device__ __forceinline__ void make_share(Share<D>& sh, int H, int head) {
+  using Sh = Share<D>;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int r_ = 0; r_ < Raw<D>::KU; ++r_) {
-    const int ui = tid + kAtThreads * r_;
-    const int key = ui / S::UPR, j = ui % S::UPR;
-    const int64_t t = t0 + key;
-    const bool ok = ui < kAtBN * S::UPR && t < Tk;
-    const int64_t row = t * H + head;
-    r.kc[r_] = ok ? kcodes[row * S::UPR + j] : 0u;
-    r.ks[r_] = ok ? (uint32_t)kscales[row * (D / 16) + (j >> 1)] : 0u;
+  for (int r = 0; r < Sh::KU; ++r) {
+    const int ui = tid + kAtThreads * r;
+    const int key = ui < kAtBN * Sh::UPR ? ui / Sh::UPR : kAtBN;
+    const int j = ui % Sh::UPR;
+    sh.kkey[r] = key;
+    const uint32_t row = (uint32_t)((key < kAtBN ? key : 0) * H + head);
+    sh.koff[r] = row * Sh::UPR + j;
+    sh.ksoff[r] = row * (D / 16) + (j >> 1);
   }
 #pragma unroll
-  for (int r_ = 0; r_ < Raw<D>::VU; ++r_) {
-    const int pi = tid + kAtThreads * r_;
-    const int j = pi / (kAtBN / 2), kp = pi % (kAtBN / 2);
+  for (int r = 0; r < Sh::VU; ++r) {
+    const int pi = tid + kAtThreads * r;
+    const bool ok = pi < (kAtBN / 2) * Sh::UPR;
+    const int j = ok ? pi / (kAtBN / 2) : 0, kp = pi % (kAtBN / 2);
+    sh.vkey[r] = ok ? 2 * kp : kAtBN;
+    sh.vj[r] = j;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int64_t t = t0 + 2 * kp + kk;
-      const bool ok = pi < (kAtBN / 2) * S::UPR && t < Tk;
-      const int64_t row = t * H + head;
-      r.vc[r_][kk] = ok ? vcodes[row * S::UPR + j] : 0u;
-      r.vs[r_][kk] = ok ? (uint32_t)vscales[row * (D / 16) + (j >> 1)] : 0u;
+      const uint32_t row = (uint32_t)((2 * kp + kk) * H + head);
+      sh.voff[r][kk] = row * Sh::UPR + j;
+      sh.vsoff[r][kk] = row * (D / 16) + (j >> 1);
     }
   }
 }
 
+// Packed K/V data of one step held in registers between its load and its dequantization.
 template <int D>
+struct Raw {
+  uint32_t kc[Share<D>::KU], ks[Share<D>::KU];
+  uint32_t vc[Share<D>::VU][2], vs[Share<D>::VU][2];
+};
+
+// Load the packed data of the step whose first key is t0; `nk` = keys present in the step
+// (64 except in the last one).  Keys past the end read as code 0 / scale 0.
+template <int D>
+__device__ __forceinline__ void load_raw(Raw<D>& r, const Share<D>& sh, int64_t t0, int nk, int H,
+                                         const uint32_t* __restrict__ kcodes,
+                                         const uint8_t* __restrict__ kscales,
+                                         const uint32_t* __restrict__ vcodes,
+                                         const uint8_t* __restrict__ vscales) {
+  const int64_t row0 = t0 * H;
+  const uint32_t* kc = kcodes + row0 * (D / 8);
+  const uint8_t* ks = kscales + row0 * (D / 16);
+  const uint32_t* vc = vcodes + row0 * (D / 8);
+  const uint8_t* vs = vscales + row0 * (D / 16);
+#pragma unroll
+  for (int i = 0; i < Share<D>::KU; ++i) {
+    const bool ok = sh.kkey[i] < nk;
+    r.kc[i] = ok ? kc[sh.koff[i]] : 0u;
+    r.ks[i] = ok ? (uint32_t)ks[sh.ksoff[i]] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < Share<D>::VU; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bool ok = sh.vkey[i] + kk < nk;
+      r.vc[i][kk] = ok ? vc[sh.voff[i][kk]] : 0u;
+      r.vs[i][kk] = ok ? (uint32_t)vs[sh.vsoff[i][kk]] : 0u;
+    }
+}
+
+// Group decode scales (A/2688) of the keys of one step.  With groups of at least kAtBN
+// tokens a step holds keys of at most two groups: keys below `split` use d0, the rest d1.
+// SHORT (groups shorter than a step) looks every key's group up.
+struct StepScales {
+  float kd0, kd1, vd0, vd1;
+  int split;
+};
+
+// Dequantize the step held in `raw` (first key t0) into one LDS buffer pair: K row-major
+// [key][d] (16 B per unit), V transposed [d][key'] with key' in vperm order inside 16-key
+// blocks, two keys per 4-byte write (vperm keeps pairs together).
+template <int D, bool SHORT>
+__device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh, int64_t t0,
+                                           const StepScales& sc, int64_t tpg,
+                                           const float* __restrict__ kamax,
+                                           const float* __restrict__ vamax, __bf16* k_buf,
+                                           __bf16* v_buf) {
+  using S = AttShape<D>;
+#pragma unroll
+  for (int i = 0; i < Share<D>::KU; ++i) {
+    const int key = sh.kkey[i];
+    if (key < kAtBN) {
+      float sd = key < sc.split ? sc.kd0 : sc.kd1;
+      if constexpr (SHORT) sd = kamax[(t0 + key) / tpg] / kGlobalDiv;
+      const int j = (int)(sh.koff[i] % S::UPR);
+      *(uint4*)(k_buf + key * S::KSTR + j * 8) = decode8(raw.kc[i], e4m3_decode(raw.ks[i]) * sd);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Share<D>::VU; ++i) {
+    const int key = sh.vkey[i];
+    if (key < kAtBN) {
+      uint4 w[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float sd = key + kk < sc.split ? sc.vd0 : sc.vd1;
+        if constexpr (SHORT) sd = vamax[(t0 + key + kk) / tpg] / kGlobalDiv;
+        w[kk] = decode8(raw.vc[i][kk], e4m3_decode(raw.vs[i][kk]) * sd);
+      }
+      const int j = sh.vj[i];
+      const int pos = (key & ~15) | vperm(key & 15);
+      const uint32_t* w0 = &w[0].x;
+      const uint32_t* w1 = &w[1].x;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {  // d = 8 j + 2 i2 and 8 j + 2 i2 + 1
+        *(uint32_t*)(v_buf + (8 * j + 2 * i2) * S::VSTR + pos) = (w0[i2] & 0xFFFFu) | (w1[i2] << 16);
+        *(uint32_t*)(v_buf + (8 * j + 2 * i2 + 1) * S::VSTR + pos) =
+            (w0[i2] >> 16) | (w1[i2] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// Tracks the group of the current step's first key as the steps advance.
+struct GroupCursor {
+  int64_t g, bnd;  // group of the step's first key, first token of the next group
+};
+
+template <bool SHORT>
+__device__ __forceinline__ StepScales step_scales(GroupCursor& gc, int64_t t0, int64_t tpg,
+                                                  int64_t n_groups, const float* __restrict__ kamax,
+                                                  const float* __restrict__ vamax) {
+  StepScales sc;
+  if constexpr (SHORT) {
+    sc.kd0 = sc.kd1 = sc.vd0 = sc.vd1 = 0.0f;
+    sc.split = kAtBN;
+  } else {
+    while (gc.bnd <= t0) {  // at most once per step when tpg >= kAtBN
+      ++gc.g;
+      gc.bnd += tpg;
+    }
+    const bool two = gc.bnd < t0 + kAtBN && gc.g + 1 < n_groups;
+    sc.split = two ? (int)(gc.bnd - t0) : kAtBN;
+    sc.kd0 = kamax[gc.g] / kGlobalDiv;
+    sc.vd0 = vamax[gc.g] / kGlobalDiv;
+    sc.kd1 = two ? kamax[gc.g + 1] / kGlobalDiv : sc.kd0;
+    sc.vd1 = two ? vamax[gc.g + 1] / kGlobalDiv : sc.vd0;
+  }
+  return sc;
+}
+
+// Software pipeline over 64-key steps with two LDS buffers: while step i runs its MFMAs on
+// buffer i%2, the packed data of step i+1 (loaded into registers one step earlier) is
+// dequantized into the other buffer and the loads for step i+2 are issued; one barrier per
+// step.
+template <int D, bool SHORT>
 __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     const uint16_t* __restrict__ q, int64_t Tq, const uint32_t* __restrict__ kcodes,
     const uint8_t* __restrict__ kscales, const float* __restrict__ kamax,
@@ -110,8 +234,8 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     const float* __restrict__ vamax, int64_t Tk, int H, int64_t tpg, int64_t n_groups,
     float qk_scale_log2, uint16_t* __restrict__ out) {
   using S = AttShape<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kAtBN * S::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[D * S::VSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kAtBN * S::KSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][D * S::VSTR];
 
   const int head = blockIdx.y;
   const int64_t q0 = (int64_t)blockIdx.x * kAtBM;
@@ -137,65 +261,23 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   // Running max (base-2 logits) and running sum.  The max is only moved when a new score
   // exceeds it by more than 8, so most steps skip the rescale of O; weights stay <= 2^8.
   float m_run = -INFINITY, l_run = 0.0f;
-  const bool short_groups = tpg < kAtBN;
 
+  Share<D> sh;
+  make_share<D>(sh, H, head);
+  GroupCursor gc = {0, tpg};
   Raw<D> raw;
-  load_raw<D>(raw, 0, Tk, H, head, kcodes, kscales, vcodes, vscales);
+  const auto keys_in = [&](int64_t t) { return (int)(Tk - t < kAtBN ? Tk - t : kAtBN); };
+  load_raw<D>(raw, sh, 0, keys_in(0), H, kcodes, kscales, vcodes, vscales);
+  stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax), tpg,
+                       kamax, vamax, k_lds[0], v_lds[0]);
+  if (kAtBN < Tk)
+    load_raw<D>(raw, sh, kAtBN, keys_in(kAtBN), H, kcodes, kscales, vcodes, vscales);
+  __syncthreads();
 
-  for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN) {
-    // Group decode scales of this step's keys: a step crosses at most one group boundary
-    // when groups are at least kAtBN tokens long; shorter groups look each key up.
-    const int64_t g0 = t0 / tpg;
-    const int64_t bnd = (g0 + 1) * tpg;
-    const bool two = bnd < t0 + kAtBN && g0 + 1 < n_groups;
-    const float kd0 = kamax[g0] / kGlobalDiv, vd0 = vamax[g0] / kGlobalDiv;
-    const float kd1 = two ? kamax[g0 + 1] / kGlobalDiv : kd0;
-    const float vd1 = two ? vamax[g0 + 1] / kGlobalDiv : vd0;
-
-    __syncthreads();  // the previous step's LDS reads are done
-    // K tile -> LDS, row-major [key][d]: 16 B per unit.
-#pragma unroll
-    for (int r_ = 0; r_ < Raw<D>::KU; ++r_) {
-      const int ui = tid + kAtThreads * r_;
-      if (ui < kAtBN * S::UPR) {
-        const int key = ui / S::UPR, j = ui % S::UPR;
-        const int64_t t = t0 + key;
-        const float sd = short_groups ? (t < Tk ? kamax[t / tpg] / kGlobalDiv : 0.0f)
-                                      : (t < bnd ? kd0 : kd1);
-        *(uint4*)(k_lds + key * S::KSTR + j * 8) = decode8(raw.kc[r_], e4m3_decode(raw.ks[r_]) * sd);
-      }
-    }
-    // V tile -> LDS transposed [d][key'], two consecutive keys per thread so that each d
-    // row gets one 4-byte write; key' = vperm order inside 16-key blocks (keeps pairs).
-#pragma unroll
-    for (int r_ = 0; r_ < Raw<D>::VU; ++r_) {
-      const int pi = tid + kAtThreads * r_;
-      if (pi < (kAtBN / 2) * S::UPR) {
-        const int j = pi / (kAtBN / 2), kp = pi % (kAtBN / 2);
-        uint4 w[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int64_t t = t0 + 2 * kp + kk;
-          const float sd = short_groups ? (t < Tk ? vamax[t / tpg] / kGlobalDiv : 0.0f)
-                                        : (t < bnd ? vd0 : vd1);
-          w[kk] = decode8(raw.vc[r_][kk], e4m3_decode(raw.vs[r_][kk]) * sd);
-        }
-        const int pos = (2 * kp & ~15) | vperm((2 * kp) & 15);
-        const uint32_t* w0 = &w[0].x;
-        const uint32_t* w1 = &w[1].x;
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {  // d = 8 j + 2 i2 and 8 j + 2 i2 + 1
-          *(uint32_t*)(v_lds + (8 * j + 2 * i2) * S::VSTR + pos) =
-              (w0[i2] & 0xFFFFu) | (w1[i2] << 16);
-          *(uint32_t*)(v_lds + (8 * j + 2 * i2 + 1) * S::VSTR + pos) =
-              (w0[i2] >> 16) | (w1[i2] & 0xFFFF0000u);
-        }
-      }
-    }
-    __syncthreads();
-    // Fetch the next step's packed K/V now; the loads complete while this step computes.
-    if (t0 + kAtBN < Tk) load_raw<D>(raw, t0 + kAtBN, Tk, H, head, kcodes, kscales, vcodes, vscales);
-
+  int buf = 0;
+  for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN, buf ^= 1) {
+    const __bf16* kb = k_lds[buf];
+    const __bf16* vb = v_lds[buf];
     // S^T = K Q^T for 64 keys (two 32-key row blocks) x the wave's 32 queries.
     f32x16 s[2];
 #pragma unroll
@@ -203,21 +285,31 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
       s[rb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < S::KCH; ++kc) {
-        const bf16x8 a = *(const bf16x8*)(k_lds + (32 * rb + l32) * S::KSTR + 16 * kc + 8 * hh);
+        const bf16x8 a = *(const bf16x8*)(kb + (32 * rb + l32) * S::KSTR + 16 * kc + 8 * hh);
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kc], s[rb], 0, 0, 0);
       }
     }
+    // Next step: dequantize into the other buffer, then start the loads of the one after.
+    if (t0 + kAtBN < Tk) {
+      const int64_t t1 = t0 + kAtBN;
+      stage_tile<D, SHORT>(raw, sh, t1, step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax),
+                           tpg, kamax, vamax, k_lds[buf ^ 1], v_lds[buf ^ 1]);
+      if (t1 + kAtBN < Tk)
+        load_raw<D>(raw, sh, t1 + kAtBN, keys_in(t1 + kAtBN), H, kcodes, kscales, vcodes, vscales);
+    }
+
     // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
     // > 0, so the max is taken on the raw scores and scaled once.  Keys past Tk (last step
     // only) are masked to -inf.
     float mx = -INFINITY;
     if (t0 + kAtBN > Tk) {
+      const int nk = (int)(Tk - t0);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = 32 * rb + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (t0 + key >= Tk) s[rb][j] = -INFINITY;
+          if (key >= nk) s[rb][j] = -INFINITY;
         }
     }
 #pragma unroll
@@ -255,11 +347,12 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
         for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[rb][8 * s2 + i];
 #pragma unroll
         for (int db = 0; db < S::DB; ++db) {
-          const bf16x8 a = *(const bf16x8*)(v_lds + (32 * db + l32) * S::VSTR + 32 * rb +
+          const bf16x8 a = *(const bf16x8*)(vb + (32 * db + l32) * S::VSTR + 32 * rb +
                                             16 * s2 + 8 * hh);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
         }
       }
+    __syncthreads();  // the other buffer is complete; this one may be overwritten next step
   }
 
   // O = O^T / l: lane l32 owns query qrow; its d values come four at a time.
@@ -311,16 +404,21 @@ extern "C" int kvfp4_attend(const uint16_t* q, int64_t q_tokens, const uint8_t* 
   const int64_t n_groups = (kv_tokens - 1) / tokens_per_group + 1;
   const float qk_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   const dim3 grid((unsigned)((q_tokens + kAtBM - 1) / kAtBM), (unsigned)heads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(kAtThreads), 0, (hipStream_t)stream, q,
-                       q_tokens, (const uint32_t*)k_codes, k_scales, k_amax,
-                       (const uint32_t*)v_codes, v_scales, v_amax, kv_tokens, (int)heads,
-                       tokens_per_group, n_groups, qk_scale_log2, out);
-  else
-    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(kAtThreads), 0, (hipStream_t)stream, q,
-                       q_tokens, (const uint32_t*)k_codes, k_scales, k_amax,
-                       (const uint32_t*)v_codes, v_scales, v_amax, kv_tokens, (int)heads,
-                       tokens_per_group, n_groups, qk_scale_log2, out);
+  const bool short_groups = tokens_per_group < kAtBN;
+  const hipStream_t st = (hipStream_t)stream;
+#define KVFP4_ATTEND_LAUNCH(D_, SHORT_)                                                           \
+  hipLaunchKernelGGL((attend_kernel<D_, SHORT_>), grid, dim3(kAtThreads), 0, st, q, q_tokens,     \
+                     (const uint32_t*)k_codes, k_scales, k_amax, (const uint32_t*)v_codes,        \
+                     v_scales, v_amax, kv_tokens, (int)heads, tokens_per_group, n_groups,         \
+                     qk_scale_log2, out)
+  if (head_dim == 128) {
+    if (short_groups) KVFP4_ATTEND_LAUNCH(128, true);
+    else KVFP4_ATTEND_LAUNCH(128, false);
+  } else {
+    if (short_groups) KVFP4_ATTEND_LAUNCH(64, true);
+    else KVFP4_ATTEND_LAUNCH(64, false);
+  }
+#undef KVFP4_ATTEND_LAUNCH
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? KVFP4_OK : set_last_hip_error((int)e);
 }
