@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvfp4_oracle.c")
-_LIB = os.path.join(_HERE, "libkvfp4_oracle.so")
+# KVFP4_ORACLE_LIB lets the mutation tests load a deliberately broken build of the oracle.
+_LIB = os.environ.get("KVFP4_ORACLE_LIB") or os.path.join(_HERE, "libkvfp4_oracle.so")
 
 RULES = {"static_6": 0, "static_4": 1, "mse": 2}
 

@@ -40,4 +40,5 @@ def load(name):
     return out
 
 
-ALL = ["w1_grid_roundtrip.txt", "w2_four_over_six.txt", "w3_outlier.txt"]
+ALL = ["w1_grid_roundtrip.txt", "w2_four_over_six.txt", "w3_outlier.txt", "w4_exact_tie.txt",
+       "w5_midpoint_ties.txt"]

@@ -74,7 +74,8 @@ def assert_parity(x_cpu_bf16, rpg, rule):
 
 # ---- worked examples through the GPU ---------------------------------------------------
 
-@pytest.mark.parametrize("name", ["w2_four_over_six.txt", "w3_outlier.txt"])
+@pytest.mark.parametrize("name", ["w2_four_over_six.txt", "w3_outlier.txt", "w4_exact_tie.txt",
+                                  "w5_midpoint_ties.txt"])
 def test_worked_examples_on_gpu(name):
     gl = goldens.load(name)
     # the library needs head_dim >= 64: pad each example row with zero blocks (a zero
