@@ -42,6 +42,8 @@ def parse_args(argv=None):
     ap.add_argument("--rule", default=None, choices=["static_6", "static_4", "mse"],
                     help="append rule (default: mse for C3, static_6 otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache gather timing (reported beside the step)")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip the fused dequantize+attention timing (reported beside the step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -112,6 +114,66 @@ class CacheWorkload:
 
     def dequant_bytes(self):
         return self.cache_elems * BYTES_PER_ELEM + 4 * self.n_groups
+
+
+class PagedWorkload:
+    """Paged cache of 30 layers x K,V x 2048 pages of 16 tokens x 12 heads x 128 (static_6),
+    physical pages in a seeded random order; the timed call gathers every page to dense bf16."""
+
+    def __init__(self, device):
+        import numpy as np
+        import torch
+
+        import kv_cache_fp4_amd as kv
+        import synth
+        cfg = synth.P1
+        self.cfg, self.kv = cfg, kv
+        D = cfg.head_dim
+        self.rpp = cfg.chunk_tokens * cfg.heads
+        self.n_blocks = cfg.layers * 2 * cfg.chunks
+        self.src = torch.cat([synth.paged_tensor(cfg, l, k, device=device).reshape(-1, D)
+                              for l in range(cfg.layers) for k in (0, 1)])
+        perm = np.random.default_rng(cfg.seed).permutation(self.n_blocks).astype(np.int32)
+        self.table = torch.from_numpy(perm).to(device)
+        self.codes = torch.empty((self.n_blocks, self.rpp, D // 2), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((self.n_blocks, self.rpp, D // 16), dtype=torch.uint8, device=device)
+        self.amax = torch.empty((self.n_blocks,), dtype=torch.float32, device=device)
+        self.out = torch.empty((self.n_blocks * self.rpp, D), dtype=torch.bfloat16, device=device)
+        kv.kvfp4_quantize_paged(self.src, self.table, self.rpp, self.codes, self.scales,
+                                self.amax, "static_6")
+        torch.cuda.synchronize(device)
+
+    def dequantize_all(self):
+        self.kv.kvfp4_dequantize_paged(self.codes, self.scales, self.amax, self.table, self.rpp,
+                                       y=self.out)
+
+    def dequant_bytes(self):
+        return self.out.numel() * BYTES_PER_ELEM + 4 * self.n_blocks
+
+
+def bench_paged(device, steps=20, warmup=3):
+    import torch
+    w = PagedWorkload(device)
+    for _ in range(warmup):
+        w.dequantize_all()
+    stream = torch.cuda.current_stream(device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize(device)
+    for a, b in ev:
+        a.record(stream)
+        w.dequantize_all()
+        b.record(stream)
+    torch.cuda.synchronize(device)
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    gbs = w.dequant_bytes() / (ms * 1e-3) / 1e9
+    res = {"workload": (f"{w.cfg.name}: gather {w.n_blocks} pages of 16 tokens x 12 heads x 128 "
+                        "(random physical order, static_6) to dense bf16"),
+           "ms_per_call": round(ms, 4), "bytes_per_call": w.dequant_bytes(),
+           "GBps": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    del w
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---- CPU baseline (oracle, single thread) -----------------------------------------------
@@ -303,6 +365,9 @@ def main(argv=None):
                       "append_bytes": w.append_bytes(),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
     }
+    if not args.no_paged:
+        print("bench: timing the paged-cache gather", file=sys.stderr, flush=True)
+        res["paged"] = bench_paged(dev)
     if not args.no_attend:
         print("bench: timing fused dequantize + attention", file=sys.stderr, flush=True)
         res["attend"] = bench_attend(dev)

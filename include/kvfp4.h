@@ -137,6 +137,35 @@ int kvfp4_attend(const uint16_t* q, int64_t q_tokens, const uint8_t* k_codes,
                  int32_t head_dim, int64_t tokens_per_group, float softmax_scale, uint16_t* out,
                  void* stream);
 
+/*
+ * Paged cache.  [P-NVFP4] "Code Implementation" / "Runtime KV-Cache De-quantization"
+ * (dequantize_kv_cache over a list of cache blocks with max_blocks, num_heads and
+ * block_token_size) and "Stage 3" (output reshaped to [block_token_size, num_heads, head_dim]).
+ *
+ * The packed cache is an array of physical pages; a page holds rows_per_page rows
+ * (block_token_size tokens x heads) and is its own scale group:
+ *   codes      uint8 [n_pages, rows_per_page, head_dim/2]; 16-byte aligned
+ *   scales     uint8 [n_pages, rows_per_page, head_dim/16]; 4-byte aligned
+ *   page_amax  float [n_pages]; 4-byte aligned
+ *   block_table int32 [n_blocks] (device): logical block b lives in page block_table[b];
+ *              entries outside [0, n_pages) are skipped (nothing is read or written for
+ *              that block); 4-byte aligned
+ * The dense side is [n_blocks * rows_per_page, head_dim] bf16, block-major (block b = rows
+ * [b*rows_per_page, (b+1)*rows_per_page)); 16-byte aligned.
+ *
+ * kvfp4_quantize_paged: quantize the dense rows block by block into their pages (group amax
+ * = the block's amax, stored in page_amax[page]).  Two blocks naming the same page race.
+ * kvfp4_dequantize_paged: gather the listed pages into dense bf16 rows; a page may be named
+ * more than once.  Same arithmetic, errors and stream rules as the unpaged calls.
+ */
+int kvfp4_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page,
+                         int32_t head_dim, int32_t rule, const int32_t* block_table,
+                         int64_t n_pages, uint8_t* codes, uint8_t* scales, float* page_amax,
+                         void* stream);
+int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scales, const float* page_amax,
+                           const int32_t* block_table, int64_t n_blocks, int64_t rows_per_page,
+                           int32_t head_dim, int64_t n_pages, uint16_t* y, void* stream);
+
 /* Host-side size helper: bytes of codes and scales and the number of group amax floats
  * for a tensor of `rows` rows.  Returns KVFP4_EINVAL / KVFP4_EUNSUPPORTED like the calls
  * above.  Any output pointer may be NULL. */

@@ -35,6 +35,10 @@ def _load() -> ctypes.CDLL:
     L.kvfp4_quantize.restype = ctypes.c_int
     L.kvfp4_dequantize.argtypes = [P, P, P, i64, i32, i64, P, P]
     L.kvfp4_dequantize.restype = ctypes.c_int
+    L.kvfp4_quantize_paged.argtypes = [P, i64, i64, i32, i32, P, i64, P, P, P, P]
+    L.kvfp4_quantize_paged.restype = ctypes.c_int
+    L.kvfp4_dequantize_paged.argtypes = [P, P, P, P, i64, i64, i32, i64, P, P]
+    L.kvfp4_dequantize_paged.restype = ctypes.c_int
     L.kvfp4_attend.argtypes = [P, i64, P, P, P, P, P, P, i64, i32, i32, i64, ctypes.c_float, P, P]
     L.kvfp4_attend.restype = ctypes.c_int
     L.kvfp4_packed_sizes.argtypes = [i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -127,6 +131,37 @@ def kvfp4_dequantize(codes, scales, group_amax, rows_per_group: int, y=None, str
     return y
 
 
+def kvfp4_quantize_paged(x, block_table, rows_per_page: int, codes, scales, page_amax,
+                         rule="static_6", stream=None):
+    """Quantize dense bf16 rows ``x`` [n_blocks*rows_per_page, head_dim] into the pages of a
+    paged cache (codes [n_pages, rows_per_page, head_dim/2], scales [..., head_dim/16],
+    page_amax [n_pages]) named by ``block_table`` (int32 [n_blocks], on the GPU)."""
+    head_dim = x.shape[-1]
+    n_blocks = block_table.numel()
+    n_pages = page_amax.numel()
+    _check(lib.kvfp4_quantize_paged(_ptr(x), n_blocks, rows_per_page, head_dim, _rule(rule),
+                                    _ptr(block_table), n_pages, _ptr(codes), _ptr(scales),
+                                    _ptr(page_amax), _stream(stream, x.device)))
+    return codes, scales, page_amax
+
+
+def kvfp4_dequantize_paged(codes, scales, page_amax, block_table, rows_per_page: int, y=None,
+                           stream=None):
+    """Gather the pages named by ``block_table`` into dense bf16 [n_blocks*rows_per_page,
+    head_dim]."""
+    import torch
+    head_dim = codes.shape[-1] * 2
+    n_blocks = block_table.numel()
+    n_pages = page_amax.numel()
+    if y is None:
+        y = torch.empty((n_blocks * rows_per_page, head_dim), dtype=torch.bfloat16,
+                        device=codes.device)
+    _check(lib.kvfp4_dequantize_paged(_ptr(codes), _ptr(scales), _ptr(page_amax),
+                                      _ptr(block_table), n_blocks, rows_per_page, head_dim,
+                                      n_pages, _ptr(y), _stream(stream, codes.device)))
+    return y
+
+
 def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
                  tokens_per_group: int, softmax_scale=None, out=None, stream=None):
     """Attention of bf16 ``q`` [q_tokens, heads, head_dim] over a packed K/V cache
@@ -148,5 +183,5 @@ def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
     return out
 
 
-__all__ = ["kvfp4_attend", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
+__all__ = ["kvfp4_attend", "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
            "lib", "LIB_PATH"]

@@ -47,26 +47,38 @@ constexpr int64_t tile_units(int threads, int unroll, int steps) {
 }
 
 // Flat partition of a tensor into (group, slice) workgroups; sizes in 8-element units.
+// With a block table (paged cache), dense group g lives in packed page table[g]; entries
+// outside [0, n_pages) are skipped.  Without one, page = group.
 struct Part {
   int64_t units_total;
   int64_t units_per_group;
   int64_t slice_units;
   uint32_t slices_per_group;
+  const int32_t* table;
+  int64_t n_pages;
 };
 
 struct Range {
-  int64_t beg, end;
-  uint32_t g;
+  int64_t beg, end;  // dense-side units [beg, end)
+  int64_t shift;     // packed-side unit = dense-side unit + shift
+  int64_t page;      // packed-side group (index of its amax)
 };
 
 __device__ __forceinline__ Range wg_range(const Part& p) {
   Range r;
-  r.g = blockIdx.x / p.slices_per_group;
-  const uint32_t s = blockIdx.x - r.g * p.slices_per_group;
-  const int64_t gbeg = (int64_t)r.g * p.units_per_group;
+  const uint32_t g = blockIdx.x / p.slices_per_group;
+  const uint32_t s = blockIdx.x - g * p.slices_per_group;
+  const int64_t gbeg = (int64_t)g * p.units_per_group;
   const int64_t gend = min(gbeg + p.units_per_group, p.units_total);
   r.beg = gbeg + (int64_t)s * p.slice_units;
   r.end = min(r.beg + p.slice_units, gend);
+  r.page = g;
+  r.shift = 0;
+  if (p.table) {
+    r.page = p.table[g];
+    if (r.page < 0 || r.page >= p.n_pages) r.end = r.beg;  // no such page: nothing to do
+    r.shift = (r.page - (int64_t)g) * p.units_per_group;
+  }
   return r;
 }
 
@@ -85,10 +97,14 @@ __device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
   __builtin_nontemporal_store(t, (u32x4*)p);
 }
 
-// ---- kernel 1: clear group amax ---------------------------------------------------------
-__global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = 0u;
+// ---- kernel 1: clear group amax (through the block table when there is one) --------------
+__global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int64_t n,
+                                                    const int32_t* __restrict__ table,
+                                                    int64_t n_pages) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t pg = table ? (int64_t)table[i] : i;
+    if (pg >= 0 && pg < n_pages) p[pg] = 0u;
+  }
 }
 
 // ---- kernel 2: group amax ([P-NVFP4] "Stage 1", global amax scalar) ---------------------
@@ -120,7 +136,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restr
 #pragma unroll
     for (int w = 1; w < kW; ++w) m = max(m, red[w]);
     // A non-negative binary32 orders like its bit pattern; bf16 -> fp32 is a 16-bit shift.
-    atomicMax(&amax_bits[r.g], m << 16);
+    atomicMax(&amax_bits[r.page], m << 16);
   }
 }
 
@@ -207,7 +223,8 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict_
                                                         uint8_t* __restrict__ scales, Part p) {
   const Range r = wg_range(p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float A = amax[r.g];
+  if (r.beg >= r.end) return;  // uniform: skipped page or empty slice
+  const float A = amax[r.page];
   const float s_enc = (A > 0.0f) ? kGlobalDiv / A : 0.0f;
   __shared__ Tables tabs;
   init_tables(&tabs, A / kGlobalDiv, THREADS);
@@ -243,8 +260,9 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict_
         pick = (err4 < err6) ? c4 : c6;
       }
       if (u < r.end) {
-        __builtin_nontemporal_store(pick.codes, codes + u);
-        if ((lane & 1) == 0) scales[u >> 1] = (uint8_t)pick.sf;
+        const int64_t pu = u + r.shift;
+        __builtin_nontemporal_store(pick.codes, codes + pu);
+        if ((lane & 1) == 0) scales[pu >> 1] = (uint8_t)pick.sf;
       }
     }
   }
@@ -258,16 +276,17 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
                                                              const float* __restrict__ amax,
                                                              uint4* __restrict__ y, Part p) {
   const Range r = wg_range(p);
+  if (r.beg >= r.end) return;  // uniform: skipped page or empty slice
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float s_dec = amax[r.g] / kGlobalDiv;
+  const float s_dec = amax[r.page] / kGlobalDiv;
   const int64_t base = r.beg + wave * 64 * kDqUnroll;
   uint32_t c[kDqUnroll], sf[kDqUnroll];
 #pragma unroll
   for (int k = 0; k < kDqUnroll; ++k) {
     const int64_t u = base + k * 64 + lane;
     const bool ok = u < r.end;
-    c[k] = ok ? codes[u] : 0u;
-    sf[k] = ok ? (uint32_t)scales[u >> 1] : 0u;
+    c[k] = ok ? codes[u + r.shift] : 0u;
+    sf[k] = ok ? (uint32_t)scales[(u + r.shift) >> 1] : 0u;
   }
 #pragma unroll
   for (int k = 0; k < kDqUnroll; ++k) {
@@ -306,6 +325,8 @@ int plan(int64_t rows, int32_t head_dim, int64_t rpg, int64_t slice, Part* part,
   part->units_per_group = upg;
   part->slice_units = slice;
   part->slices_per_group = (uint32_t)spg;
+  part->table = nullptr;
+  part->n_pages = ng;
   *grid = (unsigned)(ng * spg);
   return KVFP4_OK;
 }
@@ -321,13 +342,63 @@ int launched() {
 
 template <int RULE, int THREADS, int UNR, int STEPS>
 int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
-                 uint8_t* codes, uint8_t* scales, const float* amax, hipStream_t s) {
+                 const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
+                 const float* amax, hipStream_t s) {
   Part part;
   unsigned grid = 0;
   int rc = plan(rows, head_dim, rpg, tile_units(THREADS, UNR, STEPS), &part, &grid);
   if (rc != KVFP4_OK) return rc;
+  part.table = table;
+  if (table) part.n_pages = n_pages;
   hipLaunchKernelGGL((quant_kernel<RULE, THREADS, UNR>), dim3(grid), dim3(THREADS), 0, s,
                      (const uint4*)x, amax, (uint32_t*)codes, scales, part);
+  return launched();
+}
+
+// Shared body of the dense and paged quantize entry points (arguments already checked).
+int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
+                  const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
+                  float* group_amax, hipStream_t s) {
+  Part apart;
+  unsigned agrid = 0;
+  int rc = plan(rows, head_dim, rpg, tile_units(kAmaxThreads, kAmaxUnroll, kAmaxSteps), &apart,
+                &agrid);
+  if (rc != KVFP4_OK) return rc;
+  apart.table = table;
+  if (table) apart.n_pages = n_pages;
+  const int64_t ng = (rows - 1) / rpg + 1;
+  const int64_t cblocks = (ng + 255) / 256;
+  const unsigned cgrid = (unsigned)(cblocks < 1024 ? cblocks : 1024);
+  hipLaunchKernelGGL(clear_kernel, dim3(cgrid), dim3(256), 0, s, (uint32_t*)group_amax, ng, table,
+                     table ? n_pages : ng);
+  if ((rc = launched()) != KVFP4_OK) return rc;
+  hipLaunchKernelGGL(amax_kernel, dim3(agrid), dim3(kAmaxThreads), 0, s, (const uint4*)x,
+                     (uint32_t*)group_amax, apart);
+  if ((rc = launched()) != KVFP4_OK) return rc;
+  switch (rule) {
+    case KVFP4_RULE_STATIC6:
+      return launch_quant<KVFP4_RULE_STATIC6, kQuantThreads, kQuantUnroll, kQuantSteps>(
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+    case KVFP4_RULE_STATIC4:
+      return launch_quant<KVFP4_RULE_STATIC4, kQuantThreads, kQuantUnroll, kQuantSteps>(
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+    default:
+      return launch_quant<KVFP4_RULE_MSE, kMseThreads, kMseUnroll, kMseSteps>(
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+  }
+}
+
+int dequantize_impl(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
+                    int64_t rows, int32_t head_dim, int64_t rpg, const int32_t* table,
+                    int64_t n_pages, uint16_t* y, hipStream_t s) {
+  Part part;
+  unsigned grid = 0;
+  int rc = plan(rows, head_dim, rpg, tile_units(kDqThreads, kDqUnroll, 1), &part, &grid);
+  if (rc != KVFP4_OK) return rc;
+  part.table = table;
+  if (table) part.n_pages = n_pages;
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, s, (const uint32_t*)codes,
+                     scales, group_amax, (uint4*)y, part);
   return launched();
 }
 
@@ -348,52 +419,72 @@ extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
                               uint8_t* scales, float* group_amax, void* stream) {
   if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
     return KVFP4_EINVAL;
-  Part apart;
-  unsigned agrid = 0;
-  int rc = plan(rows, head_dim, rows_per_group, tile_units(kAmaxThreads, kAmaxUnroll, kAmaxSteps),
-                &apart, &agrid);
+  int64_t ng = 0;
+  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!x || !codes || !scales || !group_amax) return KVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4))
     return KVFP4_EALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t ng = (rows - 1) / rows_per_group + 1;
-  const int64_t cblocks = (ng + 255) / 256;
-  const unsigned cgrid = (unsigned)(cblocks < 1024 ? cblocks : 1024);
-  hipLaunchKernelGGL(clear_kernel, dim3(cgrid), dim3(256), 0, s, (uint32_t*)group_amax, ng);
-  if ((rc = launched()) != KVFP4_OK) return rc;
-  hipLaunchKernelGGL(amax_kernel, dim3(agrid), dim3(kAmaxThreads), 0, s, (const uint4*)x,
-                     (uint32_t*)group_amax, apart);
-  if ((rc = launched()) != KVFP4_OK) return rc;
-  switch (rule) {
-    case KVFP4_RULE_STATIC6:
-      return launch_quant<KVFP4_RULE_STATIC6, kQuantThreads, kQuantUnroll, kQuantSteps>(
-          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
-    case KVFP4_RULE_STATIC4:
-      return launch_quant<KVFP4_RULE_STATIC4, kQuantThreads, kQuantUnroll, kQuantSteps>(
-          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
-    default:
-      return launch_quant<KVFP4_RULE_MSE, kMseThreads, kMseUnroll, kMseSteps>(
-          x, rows, head_dim, rows_per_group, codes, scales, group_amax, s);
-  }
+  return quantize_impl(x, rows, head_dim, rows_per_group, rule, nullptr, 0, codes, scales,
+                       group_amax, (hipStream_t)stream);
 }
 
 extern "C" int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                 const float* group_amax, int64_t rows, int32_t head_dim,
                                 int64_t rows_per_group, uint16_t* y, void* stream) {
-  Part part;
-  unsigned grid = 0;
-  int rc = plan(rows, head_dim, rows_per_group, tile_units(kDqThreads, kDqUnroll, 1), &part,
-                &grid);
+  int64_t ng = 0;
+  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!codes || !scales || !group_amax || !y) return KVFP4_EINVAL;
   if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4) || !aligned(y, 16))
     return KVFP4_EALIGN;
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, (hipStream_t)stream,
-                     (const uint32_t*)codes, scales, group_amax, (uint4*)y, part);
-  return launched();
+  return dequantize_impl(codes, scales, group_amax, rows, head_dim, rows_per_group, nullptr, 0, y,
+                         (hipStream_t)stream);
+}
+
+// Paged cache: shared checks of the two paged entry points.
+static int check_paged(int64_t n_blocks, int64_t rows_per_page, int32_t head_dim, int64_t n_pages,
+                       const int32_t* block_table) {
+  if (n_blocks < 0 || rows_per_page <= 0 || n_pages < 0) return KVFP4_EINVAL;
+  if (n_blocks > 0 && (rows_per_page > (INT64_C(1) << 52) / n_blocks)) return KVFP4_EINVAL;
+  int64_t ng = 0;
+  int rc = check_shape(n_blocks * rows_per_page, head_dim, rows_per_page, &ng);
+  if (rc != KVFP4_OK) return rc;
+  if (n_blocks > 0 && !block_table) return KVFP4_EINVAL;
+  if (n_blocks > 0 && !aligned(block_table, 4)) return KVFP4_EALIGN;
+  return KVFP4_OK;
+}
+
+extern "C" int kvfp4_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page,
+                                    int32_t head_dim, int32_t rule, const int32_t* block_table,
+                                    int64_t n_pages, uint8_t* codes, uint8_t* scales,
+                                    float* page_amax, void* stream) {
+  if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
+    return KVFP4_EINVAL;
+  int rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
+  if (rc != KVFP4_OK) return rc;
+  if (n_blocks == 0) return KVFP4_OK;
+  if (!x || !codes || !scales || !page_amax) return KVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4))
+    return KVFP4_EALIGN;
+  return quantize_impl(x, n_blocks * rows_per_page, head_dim, rows_per_page, rule, block_table,
+                       n_pages, codes, scales, page_amax, (hipStream_t)stream);
+}
+
+extern "C" int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scales,
+                                      const float* page_amax, const int32_t* block_table,
+                                      int64_t n_blocks, int64_t rows_per_page, int32_t head_dim,
+                                      int64_t n_pages, uint16_t* y, void* stream) {
+  int rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
+  if (rc != KVFP4_OK) return rc;
+  if (n_blocks == 0) return KVFP4_OK;
+  if (!codes || !scales || !page_amax || !y) return KVFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4) || !aligned(y, 16))
+    return KVFP4_EALIGN;
+  return dequantize_impl(codes, scales, page_amax, n_blocks * rows_per_page, head_dim,
+                         rows_per_page, block_table, n_pages, y, (hipStream_t)stream);
 }
 
 extern "C" int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,

@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.kvfp4_oracle_dequantize.restype = i32
         L.kvfp4_oracle_attend_rows.argtypes = [P, P, P, i64, i32, i32, f64, P, i64, P, P]
         L.kvfp4_oracle_attend_rows.restype = i32
+        L.kvfp4_oracle_quantize_paged.argtypes = [P, i64, i64, i32, i32, P, i64, P, P, P]
+        L.kvfp4_oracle_quantize_paged.restype = i32
+        L.kvfp4_oracle_dequantize_paged.argtypes = [P, P, P, P, i64, i64, i32, i64, P]
+        L.kvfp4_oracle_dequantize_paged.restype = i32
         for name in ("kvfp4_oracle_e2m1_encode_n", "kvfp4_oracle_e4m3_encode_n",
                      "kvfp4_oracle_float_to_bf16_n"):
             getattr(L, name).argtypes = [P, i64, P]
@@ -184,6 +188,42 @@ def dequantize_rows(codes: np.ndarray, scales: np.ndarray, amax: float) -> np.nd
     rc = lib().kvfp4_oracle_dequantize_rows(_p(codes), _p(scales), rows, d, float(amax), _p(y))
     if rc:
         raise ValueError("oracle dequantize_rows: bad arguments")
+    return y
+
+
+def quantize_paged(x_bf16: np.ndarray, table: np.ndarray, rows_per_page: int, n_pages: int,
+                   rule="static_6", codes=None, scales=None, page_amax=None):
+    """Dense x [n_blocks*rows_per_page, d] into pages named by table (int32 [n_blocks]).
+    Pages not named keep the contents of the given (or zero) buffers."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    d = x.shape[1]
+    if codes is None:
+        codes = np.zeros((n_pages, rows_per_page, d // 2), np.uint8)
+    if scales is None:
+        scales = np.zeros((n_pages, rows_per_page, d // 16), np.uint8)
+    if page_amax is None:
+        page_amax = np.zeros(n_pages, np.float32)
+    rc = lib().kvfp4_oracle_quantize_paged(_p(x), table.size, rows_per_page, d, _rule(rule),
+                                           _p(table), n_pages, _p(codes), _p(scales),
+                                           _p(page_amax))
+    if rc:
+        raise ValueError("oracle quantize_paged: bad arguments")
+    return codes, scales, page_amax
+
+
+def dequantize_paged(codes, scales, page_amax, table, rows_per_page: int, y=None):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    page_amax = np.ascontiguousarray(page_amax, dtype=np.float32)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    d = codes.shape[-1] * 2
+    if y is None:
+        y = np.zeros((table.size * rows_per_page, d), np.uint16)
+    rc = lib().kvfp4_oracle_dequantize_paged(_p(codes), _p(scales), _p(page_amax), _p(table),
+                                             table.size, rows_per_page, d, page_amax.size, _p(y))
+    if rc:
+        raise ValueError("oracle dequantize_paged: bad arguments")
     return y
 
 

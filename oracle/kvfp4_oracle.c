@@ -284,6 +284,45 @@ int kvfp4_oracle_dequantize(const uint8_t* codes, const uint8_t* scales,
 }
 
 /* ------------------------------------------------------------------------------------
+ * Paged cache.  [P-NVFP4] "Code Implementation" / "Runtime KV-Cache De-quantization" (the
+ * cache as a list of blocks of block_token_size tokens, gathered for attention) and "Stage 3"
+ * (each block reshaped to [block_token_size, num_heads, head_dim]).  A page is one scale
+ * group; logical block b lives in page table[b]; entries outside [0, n_pages) are skipped.
+ * ---------------------------------------------------------------------------------- */
+int kvfp4_oracle_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page, int d,
+                                int rule, const int32_t* table, int64_t n_pages, uint8_t* codes,
+                                uint8_t* scales, float* page_amax) {
+  if (n_blocks < 0 || rows_per_page <= 0 || d <= 0 || d % 16 != 0) return 1;
+  for (int64_t b = 0; b < n_blocks; ++b) {
+    int64_t pg = table[b];
+    if (pg < 0 || pg >= n_pages) continue;
+    const uint16_t* xb = x + b * rows_per_page * d;
+    float A = kvfp4_oracle_group_amax(xb, rows_per_page * d);
+    page_amax[pg] = A;
+    int rc = kvfp4_oracle_quantize_rows(xb, rows_per_page, d, A, rule,
+                                        codes + pg * rows_per_page * (d / 2),
+                                        scales + pg * rows_per_page * (d / 16));
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int kvfp4_oracle_dequantize_paged(const uint8_t* codes, const uint8_t* scales,
+                                  const float* page_amax, const int32_t* table, int64_t n_blocks,
+                                  int64_t rows_per_page, int d, int64_t n_pages, uint16_t* y) {
+  if (n_blocks < 0 || rows_per_page <= 0 || d <= 0 || d % 16 != 0) return 1;
+  for (int64_t b = 0; b < n_blocks; ++b) {
+    int64_t pg = table[b];
+    if (pg < 0 || pg >= n_pages) continue;
+    int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),
+                                          scales + pg * rows_per_page * (d / 16), rows_per_page,
+                                          d, page_amax[pg], y + b * rows_per_page * d);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
  * Attention over a dequantized cache.  [P-KV] "CUDA De-quantization Pipeline" (the bf16
  * K/V reconstructed before attention feed the attention operation); [P-SF] Table 3 (the
  * active cache is dequantized to dense BF16 before attention).  The operation itself is

@@ -125,6 +125,20 @@ C5_Q_TOKENS = 4680
 
 CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
 
+# Paged cache: the pages' dequantize_kv_cache example uses 16-token blocks; here a
+# full-cache-sized paged cache of 30 layers x K,V x 2048 pages of 16 tokens (32768 tokens)
+# x 12 heads x 128, values as the full-cache workload (channel log-normal).
+P1 = CacheConfig("paged_30Lx2048px16x12x128", layers=30, heads=12, head_dim=128,
+                 chunk_tokens=16, chunks=2048, seed=6)
+
+
+def paged_tensor(cfg: CacheConfig, layer: int, kv: int, device="cpu"):
+    """bf16 [chunks * chunk_tokens, heads, head_dim] of one layer's K or V (all its pages)."""
+    f = channel_factors(cfg.heads, cfg.head_dim, sub_seed(cfg.seed, layer, kv, 1 << 20),
+                        device=device)
+    return channel_lognormal(cfg.chunks * cfg.chunk_tokens, cfg.heads, cfg.head_dim,
+                             sub_seed(cfg.seed, layer, kv, 0), f, device=device)
+
 
 def chunk_group(cfg: CacheConfig, layer: int, kv: int, chunk: int, device="cpu"):
     """bf16 [chunk_tokens, heads, head_dim] for one (layer, K/V, chunk) scale group."""

@@ -132,3 +132,36 @@ def test_attend_rejects(kw, want):
 
 def test_attend_zero_queries_is_a_noop():
     assert at(tq=0, q=None, kc=None, ks=None, ka=None, vc=None, vs=None, va=None, out=None) == KVFP4_OK
+
+
+def qp(x=A16, nb=4, rpp=24, d=128, rule=0, tab=A16, npg=8, codes=A16, scales=A16, amax=A16):
+    return lib.kvfp4_quantize_paged(x, nb, rpp, d, rule, tab, npg, codes, scales, amax, None)
+
+
+def dqp(codes=A16, scales=A16, amax=A16, tab=A16, nb=4, rpp=24, d=128, npg=8, y=A16):
+    return lib.kvfp4_dequantize_paged(codes, scales, amax, tab, nb, rpp, d, npg, y, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=-1), KVFP4_EINVAL), (dict(rpp=0), KVFP4_EINVAL), (dict(npg=-1), KVFP4_EINVAL),
+    (dict(rule=5), KVFP4_EINVAL), (dict(tab=None), KVFP4_EINVAL), (dict(x=None), KVFP4_EINVAL),
+    (dict(d=100), KVFP4_EUNSUPPORTED), (dict(tab=A16 + 2), KVFP4_EALIGN),
+    (dict(codes=A16 + 8), KVFP4_EALIGN), (dict(amax=A16 + 1), KVFP4_EALIGN),
+    (dict(nb=1 << 40, rpp=1 << 20), KVFP4_EINVAL),
+])
+def test_quantize_paged_rejects(kw, want):
+    assert qp(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=-1), KVFP4_EINVAL), (dict(rpp=-2), KVFP4_EINVAL), (dict(tab=None), KVFP4_EINVAL),
+    (dict(y=None), KVFP4_EINVAL), (dict(d=32), KVFP4_EUNSUPPORTED), (dict(y=A16 + 4), KVFP4_EALIGN),
+    (dict(scales=A16 + 3), KVFP4_EALIGN),
+])
+def test_dequantize_paged_rejects(kw, want):
+    assert dqp(**kw) == want
+
+
+def test_paged_zero_blocks_is_a_noop():
+    assert qp(nb=0, x=None, tab=None, codes=None, scales=None, amax=None) == KVFP4_OK
+    assert dqp(nb=0, codes=None, scales=None, amax=None, tab=None, y=None) == KVFP4_OK

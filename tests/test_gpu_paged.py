@@ -1,0 +1,82 @@
+"""GPU parity of the paged-cache entry points against the oracle (bit for bit): permuted
+block tables with spare pages, skipped entries, pages gathered twice, every rule, and a
+full-size paged cache (16-token pages, 12 heads, 128 dims) on sampled pages."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("rule", ["static_6", "static_4", "mse"])
+@pytest.mark.parametrize("nb,rpp,d", [(37, 16 * 12, 128), (5, 64, 64), (200, 16 * 4, 256)])
+def test_paged_round_trip_matches_oracle(rule, nb, rpp, d):
+    import kv_cache_fp4_amd as kv
+    npg = nb + 7
+    x = synth.gauss_outliers((nb * rpp, d), seed=nb + rpp + d)
+    tab = np.random.default_rng(nb).permutation(npg)[:nb].astype(np.int32)
+    codes = torch.full((npg, rpp, d // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((npg, rpp, d // 16), 0x33, dtype=torch.uint8, device=DEV)
+    amax = torch.full((npg,), -3.0, dtype=torch.float32, device=DEV)
+    ttab = torch.from_numpy(tab).to(DEV)
+    kv.kvfp4_quantize_paged(x.to(DEV), ttab, rpp, codes, scales, amax, rule)
+    y = kv.kvfp4_dequantize_paged(codes, scales, amax, ttab, rpp)
+    torch.cuda.synchronize()
+    oc = np.full((npg, rpp, d // 2), 0x5A, np.uint8)
+    os_ = np.full((npg, rpp, d // 16), 0x33, np.uint8)
+    oa = np.full(npg, -3.0, np.float32)
+    oracle.quantize_paged(_u16(x), tab, rpp, npg, rule, oc, os_, oa)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(amax.cpu().numpy(), oa)
+    assert np.array_equal(_u16(y), oracle.dequantize_paged(oc, os_, oa, tab, rpp))
+
+
+def test_paged_gather_skips_and_repeats():
+    import kv_cache_fp4_amd as kv
+    nb, rpp, d = 6, 192, 128
+    x = synth.gauss_outliers((nb * rpp, d), seed=3)
+    tab = np.arange(nb, dtype=np.int32)
+    ttab = torch.from_numpy(tab).to(DEV)
+    codes = torch.zeros((nb, rpp, d // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((nb, rpp, d // 16), dtype=torch.uint8, device=DEV)
+    amax = torch.zeros((nb,), dtype=torch.float32, device=DEV)
+    kv.kvfp4_quantize_paged(x.to(DEV), ttab, rpp, codes, scales, amax, "mse")
+    gather = np.array([5, -1, 5, nb, 0, 2, 2], dtype=np.int32)
+    y = torch.full((gather.size * rpp, d), 0x1234, dtype=torch.int16, device=DEV)
+    kv.kvfp4_dequantize_paged(codes, scales, amax, torch.from_numpy(gather).to(DEV), rpp,
+                              y=y.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    oc, os_, oa = oracle.quantize_paged(_u16(x), tab, rpp, nb, "mse")
+    want = oracle.dequantize_paged(oc, os_, oa, gather, rpp,
+                                   y=np.full((gather.size * rpp, d), 0x1234, np.uint16))
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), want)
+
+
+def test_full_size_paged_cache_sampled():
+    """30 layers x K,V x 2048 pages of 16 tokens (32768 tokens) x 12 heads x 128, pages in a
+    random physical order; 6 sampled pages recomputed by the oracle from the same inputs."""
+    import bench
+    w = bench.PagedWorkload(DEV)
+    w.dequantize_all()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    tab = w.table.cpu().numpy()
+    for b in [0, w.n_blocks - 1] + list(rng.integers(0, w.n_blocks, 4)):
+        r0 = int(b) * w.rpp
+        xb = _u16(w.src[r0:r0 + w.rpp])
+        pg = int(tab[b])
+        oc, os_, oa = oracle.quantize_paged(xb, np.array([0], np.int32), w.rpp, 1, "static_6")
+        assert np.array_equal(w.codes[pg].cpu().numpy(), oc[0])
+        assert np.array_equal(w.scales[pg].cpu().numpy(), os_[0])
+        assert w.amax[pg].item() == oa[0]
+        assert np.array_equal(_u16(w.out[r0:r0 + w.rpp]),
+                              oracle.dequantize_rows(oc[0], os_[0], oa[0]))
