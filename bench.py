@@ -42,6 +42,8 @@ def parse_args(argv=None):
     ap.add_argument("--rule", default=None, choices=["static_6", "static_4", "mse"],
                     help="append rule (default: mse for C3, static_6 otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rtn", action="store_true",
+                    help="skip the RTN INT4/INT2 timing (reported beside the step)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache gather timing (reported beside the step)")
     ap.add_argument("--no-attend", action="store_true",
@@ -172,6 +174,47 @@ def bench_paged(device, steps=20, warmup=3):
            "ms_per_call": round(ms, 4), "bytes_per_call": w.dequant_bytes(),
            "GBps": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     del w
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_rtn(device, steps=20, warmup=3):
+    """RTN INT4 and INT2 caches of the full-cache size (30 x 2 x 32760 x 12 x 128 elements,
+    one tensor): quantize and dequantize rates.  Algorithmic bytes per element: 2 (bf16) +
+    bits/8 (codes) + 2/16 (bf16 block scale)."""
+    import torch
+
+    import kv_cache_fp4_amd as kv
+    import synth
+    cfg = synth.C3
+    rows = cfg.layers * 2 * cfg.cache_tokens * cfg.heads
+    g = torch.Generator(device=device).manual_seed(7)
+    x = torch.randn((rows, cfg.head_dim), generator=g, device=device).to(torch.bfloat16)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(device)
+    res = {"workload": f"rtn_full_cache_{rows}x{cfg.head_dim}: symmetric blockwise RTN, block 16"}
+    for bits in (4, 2):
+        codes, scales = kv.kvfp4_rtn_quantize(x, bits)
+        per = 2.0 + bits / 8.0 + 2.0 / 16.0
+        nbytes = x.numel() * per
+        for name, fn in (("quantize", lambda: kv.kvfp4_rtn_quantize(x, bits, codes, scales)),
+                         ("dequantize", lambda: kv.kvfp4_rtn_dequantize(codes, scales, bits, y=out))):
+            for _ in range(warmup):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            torch.cuda.synchronize(device)
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize(device)
+            ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            res[f"int{bits}_{name}"] = {"ms": round(ms, 4), "GBps": round(gbs, 2),
+                                        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        del codes, scales
+    del x, out
     torch.cuda.empty_cache()
     return res
 
@@ -365,6 +408,9 @@ def main(argv=None):
                       "append_bytes": w.append_bytes(),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
     }
+    if not args.no_rtn:
+        print("bench: timing the RTN INT4/INT2 caches", file=sys.stderr, flush=True)
+        res["rtn"] = bench_rtn(dev)
     if not args.no_paged:
         print("bench: timing the paged-cache gather", file=sys.stderr, flush=True)
         res["paged"] = bench_paged(dev)

@@ -166,6 +166,33 @@ int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scales, const fl
                            const int32_t* block_table, int64_t n_blocks, int64_t rows_per_page,
                            int32_t head_dim, int64_t n_pages, uint16_t* y, void* stream);
 
+/*
+ * Round-to-nearest symmetric blockwise integer quantization (INT4 or INT2) -- the RTN
+ * baselines of [P-SF] Table 3: RTN_INT4, RTN_INT2, RTN_K2_V4 (2-bit keys, 4-bit values: two
+ * calls with different `bits`) and RTN_INT4 RECENT2 (the newest frame-blocks stay bf16 and
+ * are copied back behind the dequantized prefix on read: `tail`).
+ *
+ * Per 16-element block along head_dim: qmax = 2^(bits-1) - 1 (7 or 1), s = bf16_rne(m/qmax)
+ * with m = max|x| (binary32 division), inv = s > 0 ? 1/s : 0, q = clamp(rne(x*inv), -qmax,
+ * qmax) stored as a two's-complement bit field, element 8k+i at bits [bits*i, bits*(i+1)) of
+ * its 8-element group (INT4: element 2j in the low nibble of byte j; INT2: element 4j+k at
+ * bits 2k of byte j); dequant = bf16_rne(q * s).  No group amax.  One 16-bit scale per 16
+ * elements: 5 bits/element (INT4), 3 bits/element (INT2, the 5.33x of [P-SF] Tables 4-5).
+ *
+ *   x       bf16 [rows, head_dim]; 16-byte aligned
+ *   bits    2 or 4 (else KVFP4_EINVAL)
+ *   codes   uint8 [rows, head_dim*bits/8]; 16-byte aligned
+ *   scales  bf16 bit patterns [rows, head_dim/16]; 4-byte aligned
+ *   tail    bf16 [tail_rows, head_dim] copied verbatim after the dequantized rows (may be
+ *           NULL when tail_rows == 0); 16-byte aligned
+ *   y (out) bf16 [rows + tail_rows, head_dim]; 16-byte aligned
+ */
+int kvfp4_rtn_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int32_t bits,
+                       uint8_t* codes, uint16_t* scales, void* stream);
+int kvfp4_rtn_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows,
+                         int32_t head_dim, int32_t bits, const uint16_t* tail, int64_t tail_rows,
+                         uint16_t* y, void* stream);
+
 /* Host-side size helper: bytes of codes and scales and the number of group amax floats
  * for a tensor of `rows` rows.  Returns KVFP4_EINVAL / KVFP4_EUNSUPPORTED like the calls
  * above.  Any output pointer may be NULL. */

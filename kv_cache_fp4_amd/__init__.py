@@ -39,6 +39,10 @@ def _load() -> ctypes.CDLL:
     L.kvfp4_quantize_paged.restype = ctypes.c_int
     L.kvfp4_dequantize_paged.argtypes = [P, P, P, P, i64, i64, i32, i64, P, P]
     L.kvfp4_dequantize_paged.restype = ctypes.c_int
+    L.kvfp4_rtn_quantize.argtypes = [P, i64, i32, i32, P, P, P]
+    L.kvfp4_rtn_quantize.restype = ctypes.c_int
+    L.kvfp4_rtn_dequantize.argtypes = [P, P, i64, i32, i32, P, i64, P, P]
+    L.kvfp4_rtn_dequantize.restype = ctypes.c_int
     L.kvfp4_attend.argtypes = [P, i64, P, P, P, P, P, P, i64, i32, i32, i64, ctypes.c_float, P, P]
     L.kvfp4_attend.restype = ctypes.c_int
     L.kvfp4_packed_sizes.argtypes = [i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -162,6 +166,35 @@ def kvfp4_dequantize_paged(codes, scales, page_amax, block_table, rows_per_page:
     return y
 
 
+def kvfp4_rtn_quantize(x, bits: int, codes=None, scales=None, stream=None):
+    """Symmetric blockwise RTN of bf16 rows ``x`` [..., head_dim]: returns (codes uint8
+    [rows, head_dim*bits/8], scales bf16 [rows, head_dim/16])."""
+    import torch
+    head_dim = x.shape[-1]
+    rows = x.numel() // head_dim if head_dim else 0
+    if codes is None:
+        codes = torch.empty((rows, head_dim * bits // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, head_dim // 16), dtype=torch.bfloat16, device=x.device)
+    _check(lib.kvfp4_rtn_quantize(_ptr(x), rows, head_dim, int(bits), _ptr(codes), _ptr(scales),
+                                  _stream(stream, x.device)))
+    return codes, scales
+
+
+def kvfp4_rtn_dequantize(codes, scales, bits: int, tail=None, y=None, stream=None):
+    """bf16 [rows + tail_rows, head_dim]: the dequantized rows followed by ``tail`` (bf16
+    [tail_rows, head_dim], the recent rows kept unquantized)."""
+    import torch
+    rows = codes.shape[0]
+    head_dim = scales.shape[1] * 16
+    tail_rows = 0 if tail is None else tail.numel() // head_dim
+    if y is None:
+        y = torch.empty((rows + tail_rows, head_dim), dtype=torch.bfloat16, device=codes.device)
+    _check(lib.kvfp4_rtn_dequantize(_ptr(codes), _ptr(scales), rows, head_dim, int(bits),
+                                    _ptr(tail), tail_rows, _ptr(y), _stream(stream, codes.device)))
+    return y
+
+
 def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
                  tokens_per_group: int, softmax_scale=None, out=None, stream=None):
     """Attention of bf16 ``q`` [q_tokens, heads, head_dim] over a packed K/V cache
@@ -183,5 +216,5 @@ def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
     return out
 
 
-__all__ = ["kvfp4_attend", "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
+__all__ = ["kvfp4_rtn_quantize", "kvfp4_rtn_dequantize", "kvfp4_attend", "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
            "lib", "LIB_PATH"]

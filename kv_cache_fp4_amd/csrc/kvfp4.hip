@@ -295,6 +295,111 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
   }
 }
 
+// ---- RTN symmetric blockwise INT4 / INT2 ([P-SF] Table 3) --------------------------------
+// Per 16-element block: s = bf16(m / qmax), inv = 1/s, q = clamp(rne(x * inv), +-qmax) in
+// two's complement, lowest element in the lowest bits; dequant bf16(q * s).  Same lane-pair
+// mapping as the NVFP4 encoder: a lane packs its 8 codes into 32 (INT4) or 16 (INT2) bits.
+template <int BITS>
+__global__ __launch_bounds__(kQuantThreads) void rtn_quant_kernel(const uint4* __restrict__ x,
+                                                                  void* __restrict__ codes,
+                                                                  uint16_t* __restrict__ scales,
+                                                                  Part p) {
+  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
+  const Range r = wg_range(p);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t base = r.beg + wave * 64 * kQuantUnroll; base < r.end;
+       base += kQuantThreads * kQuantUnroll) {
+    uint4 v[kQuantUnroll];
+#pragma unroll
+    for (int k = 0; k < kQuantUnroll; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      v[k] = (u < r.end) ? x[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kQuantUnroll; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      const float xf[8] = {bf16_lo(v[k].x), bf16_hi(v[k].x), bf16_lo(v[k].y), bf16_hi(v[k].y),
+                           bf16_lo(v[k].z), bf16_hi(v[k].z), bf16_lo(v[k].w), bf16_hi(v[k].w)};
+      uint32_t mb = absmax8_bits(v[k]);
+      mb = max(mb, swap_pair(mb));
+      const float m = __uint_as_float(mb << 16);
+      const float sq = (BITS == 4) ? m / kQmax : m;  // IEEE division; m/1 is m
+      const uint32_t sh = pack_bf16x2(sq, 0.0f) & 0xFFFFu;
+      const float sv = __uint_as_float(sh << 16);
+      const float inv = (sv > 0.0f) ? 1.0f / sv : 0.0f;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float qf = fminf(fmaxf(__builtin_rintf(xf[i] * inv), -kQmax), kQmax);
+        w |= ((uint32_t)(int)qf & ((1u << BITS) - 1)) << (BITS * i);
+      }
+      if (u < r.end) {
+        if constexpr (BITS == 4) ((uint32_t*)codes)[u] = w;
+        else ((uint16_t*)codes)[u] = (uint16_t)w;
+        if ((lane & 1) == 0) scales[u >> 1] = (uint16_t)sh;
+      }
+    }
+  }
+}
+
+// Dequantize a packed prefix of `prefix_units` units, then copy a bf16 tail (the recent,
+// unquantized rows) behind it in the same launch.
+template <int BITS>
+__global__ __launch_bounds__(kDqThreads) void rtn_dequant_kernel(const void* __restrict__ codes,
+                                                                 const uint16_t* __restrict__ scales,
+                                                                 const uint4* __restrict__ tail,
+                                                                 int64_t prefix_units,
+                                                                 uint4* __restrict__ y, Part p) {
+  const Range r = wg_range(p);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = r.beg + wave * 64 * kDqUnroll;
+  if (r.beg >= prefix_units) {  // uniform: a workgroup of the bf16 tail only
+    uint4 t[kDqUnroll];
+#pragma unroll
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      t[k] = u < r.end ? tail[u - prefix_units] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      if (u < r.end) store_nt(y + u, t[k]);
+    }
+    return;
+  }
+  // Packed prefix (a workgroup may also hold the first tail units: handled per lane).
+  uint32_t w[kDqUnroll], sb[kDqUnroll];
+#pragma unroll
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t u = base + k * 64 + lane;
+    const bool ok = u < r.end && u < prefix_units;
+    w[k] = ok ? ((BITS == 4) ? ((const uint32_t*)codes)[u] : (uint32_t)((const uint16_t*)codes)[u]) : 0u;
+    sb[k] = ok ? (uint32_t)scales[u >> 1] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t u = base + k * 64 + lane;
+    if (u >= r.end) continue;
+    uint4 o;
+    if (u < prefix_units) {
+      const float sv = __uint_as_float(sb[k] << 16);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = (int)(w[k] << (32 - BITS * (i + 1))) >> (32 - BITS);  // sign-extend field i
+        f[i] = (float)q * sv;
+      }
+      o.x = pack_bf16x2(f[0], f[1]);
+      o.y = pack_bf16x2(f[2], f[3]);
+      o.z = pack_bf16x2(f[4], f[5]);
+      o.w = pack_bf16x2(f[6], f[7]);
+    } else {
+      o = tail[u - prefix_units];
+    }
+    store_nt(y + u, o);
+  }
+}
+
 // ---- host side ----------------------------------------------------------------------------
 
 thread_local int g_last_hip_error = 0;
@@ -485,6 +590,52 @@ extern "C" int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scale
     return KVFP4_EALIGN;
   return dequantize_impl(codes, scales, page_amax, n_blocks * rows_per_page, head_dim,
                          rows_per_page, block_table, n_pages, y, (hipStream_t)stream);
+}
+
+extern "C" int kvfp4_rtn_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int32_t bits,
+                                  uint8_t* codes, uint16_t* scales, void* stream) {
+  if (bits != 2 && bits != 4) return KVFP4_EINVAL;
+  Part part;
+  unsigned grid = 0;
+  int rc = plan(rows, head_dim, rows > 0 ? rows : 1, tile_units(kQuantThreads, kQuantUnroll, 1),
+                &part, &grid);
+  if (rc != KVFP4_OK) return rc;
+  if (rows == 0) return KVFP4_OK;
+  if (!x || !codes || !scales) return KVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return KVFP4_EALIGN;
+  if (bits == 4)
+    hipLaunchKernelGGL(rtn_quant_kernel<4>, dim3(grid), dim3(kQuantThreads), 0, (hipStream_t)stream,
+                       (const uint4*)x, (void*)codes, scales, part);
+  else
+    hipLaunchKernelGGL(rtn_quant_kernel<2>, dim3(grid), dim3(kQuantThreads), 0, (hipStream_t)stream,
+                       (const uint4*)x, (void*)codes, scales, part);
+  return launched();
+}
+
+extern "C" int kvfp4_rtn_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows,
+                                    int32_t head_dim, int32_t bits, const uint16_t* tail,
+                                    int64_t tail_rows, uint16_t* y, void* stream) {
+  if (bits != 2 && bits != 4) return KVFP4_EINVAL;
+  if (rows < 0 || tail_rows < 0 || rows > INT64_MAX / 2 - tail_rows) return KVFP4_EINVAL;
+  const int64_t total = rows + tail_rows;
+  Part part;
+  unsigned grid = 0;
+  int rc = plan(total, head_dim, total > 0 ? total : 1, tile_units(kDqThreads, kDqUnroll, 1), &part,
+                &grid);
+  if (rc != KVFP4_OK) return rc;
+  if (total == 0) return KVFP4_OK;
+  if (!y || (rows > 0 && (!codes || !scales)) || (tail_rows > 0 && !tail)) return KVFP4_EINVAL;
+  if (!aligned(y, 16) || (rows > 0 && (!aligned(codes, 16) || !aligned(scales, 4))) ||
+      (tail_rows > 0 && !aligned(tail, 16)))
+    return KVFP4_EALIGN;
+  const int64_t prefix_units = rows * (head_dim / 8);
+  if (bits == 4)
+    hipLaunchKernelGGL(rtn_dequant_kernel<4>, dim3(grid), dim3(kDqThreads), 0, (hipStream_t)stream,
+                       (const void*)codes, scales, (const uint4*)tail, prefix_units, (uint4*)y, part);
+  else
+    hipLaunchKernelGGL(rtn_dequant_kernel<2>, dim3(grid), dim3(kDqThreads), 0, (hipStream_t)stream,
+                       (const void*)codes, scales, (const uint4*)tail, prefix_units, (uint4*)y, part);
+  return launched();
 }
 
 extern "C" int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,

@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.kvfp4_oracle_quantize_paged.restype = i32
         L.kvfp4_oracle_dequantize_paged.argtypes = [P, P, P, P, i64, i64, i32, i64, P]
         L.kvfp4_oracle_dequantize_paged.restype = i32
+        L.kvfp4_oracle_rtn_quantize.argtypes = [P, i64, i32, i32, P, P]
+        L.kvfp4_oracle_rtn_quantize.restype = i32
+        L.kvfp4_oracle_rtn_dequantize.argtypes = [P, P, i64, i32, i32, P]
+        L.kvfp4_oracle_rtn_dequantize.restype = i32
         for name in ("kvfp4_oracle_e2m1_encode_n", "kvfp4_oracle_e4m3_encode_n",
                      "kvfp4_oracle_float_to_bf16_n"):
             getattr(L, name).argtypes = [P, i64, P]
@@ -224,6 +228,28 @@ def dequantize_paged(codes, scales, page_amax, table, rows_per_page: int, y=None
                                              table.size, rows_per_page, d, page_amax.size, _p(y))
     if rc:
         raise ValueError("oracle dequantize_paged: bad arguments")
+    return y
+
+
+def rtn_quantize(x_bf16: np.ndarray, bits: int):
+    """Symmetric blockwise RTN: codes u8 [rows, d*bits/8], scales bf16 bits u16 [rows, d/16]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, d = x.shape
+    codes = np.zeros((rows, d * bits // 8), np.uint8)
+    scales = np.zeros((rows, d // 16), np.uint16)
+    if lib().kvfp4_oracle_rtn_quantize(_p(x), rows, d, bits, _p(codes), _p(scales)):
+        raise ValueError("oracle rtn_quantize: bad arguments")
+    return codes, scales
+
+
+def rtn_dequantize(codes: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    rows = codes.shape[0]
+    d = codes.shape[1] * 8 // bits
+    y = np.zeros((rows, d), np.uint16)
+    if lib().kvfp4_oracle_rtn_dequantize(_p(codes), _p(scales), rows, d, bits, _p(y)):
+        raise ValueError("oracle rtn_dequantize: bad arguments")
     return y
 
 

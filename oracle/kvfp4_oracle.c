@@ -323,6 +323,66 @@ int kvfp4_oracle_dequantize_paged(const uint8_t* codes, const uint8_t* scales,
 }
 
 /* ------------------------------------------------------------------------------------
+ * Round-to-nearest symmetric blockwise integer quantization.  [P-SF] Table 3 (RTN_INT2,
+ * RTN_INT4, RTN_K2_V4, RTN_INT4 RECENT2: symmetric blockwise quantization of K and V,
+ * block_size=16, packed storage plus per-block scales; on read the quantized prefix is
+ * dequantized and the bf16 recent tail copied back in).
+ * Per 16-element block: qmax = 2^(bits-1) - 1; s = bf16(m / qmax) with m = max |x|;
+ * inv = s > 0 ? 1/s : 0; q = clamp(nearest-even(x * inv), -qmax, qmax) in two's complement,
+ * element 2j (INT4) or 4j+k (INT2) in the lowest bits first; dequant = bf16(q * s).
+ * ---------------------------------------------------------------------------------- */
+int kvfp4_oracle_rtn_quantize(const uint16_t* x, int64_t rows, int d, int bits, uint8_t* codes,
+                              uint16_t* scales) {
+  if (rows < 0 || d <= 0 || d % 16 != 0 || (bits != 2 && bits != 4)) return 1;
+  const int qmax = (1 << (bits - 1)) - 1;
+  const int per_byte = 8 / bits;
+  const int nb = d / 16;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      float xb[16];
+      float m = 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        xb[i] = kvfp4_oracle_bf16_to_float(x[r * d + b * 16 + i]);
+        if (fabsf(xb[i]) > m) m = fabsf(xb[i]);
+      }
+      uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);
+      float sv = kvfp4_oracle_bf16_to_float(sh);
+      float inv = (sv > 0.0f) ? 1.0f / sv : 0.0f;
+      scales[r * nb + b] = sh;
+      for (int i = 0; i < 16; ++i) {
+        float v = rintf(xb[i] * inv);
+        if (v > (float)qmax) v = (float)qmax;
+        if (v < (float)-qmax) v = (float)-qmax;
+        int q = (int)v;
+        int e = b * 16 + i;
+        uint8_t* byte = &codes[r * (d * bits / 8) + e / per_byte];
+        int shift = (e % per_byte) * bits;
+        if (shift == 0) *byte = 0;
+        *byte |= (uint8_t)((q & ((1 << bits) - 1)) << shift);
+      }
+    }
+  }
+  return 0;
+}
+
+int kvfp4_oracle_rtn_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows, int d,
+                                int bits, uint16_t* y) {
+  if (rows < 0 || d <= 0 || d % 16 != 0 || (bits != 2 && bits != 4)) return 1;
+  const int per_byte = 8 / bits;
+  const int nb = d / 16;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int e = 0; e < d; ++e) {
+      float sv = kvfp4_oracle_bf16_to_float(scales[r * nb + e / 16]);
+      int raw = (codes[r * (d * bits / 8) + e / per_byte] >> ((e % per_byte) * bits)) &
+                ((1 << bits) - 1);
+      int q = (raw >= (1 << (bits - 1))) ? raw - (1 << bits) : raw;
+      y[r * d + e] = kvfp4_oracle_float_to_bf16((float)q * sv);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
  * Attention over a dequantized cache.  [P-KV] "CUDA De-quantization Pipeline" (the bf16
  * K/V reconstructed before attention feed the attention operation); [P-SF] Table 3 (the
  * active cache is dequantized to dense BF16 before attention).  The operation itself is

@@ -165,3 +165,30 @@ def test_dequantize_paged_rejects(kw, want):
 def test_paged_zero_blocks_is_a_noop():
     assert qp(nb=0, x=None, tab=None, codes=None, scales=None, amax=None) == KVFP4_OK
     assert dqp(nb=0, codes=None, scales=None, amax=None, tab=None, y=None) == KVFP4_OK
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(bits=3), KVFP4_EINVAL), (dict(bits=8), KVFP4_EINVAL), (dict(rows=-1), KVFP4_EINVAL),
+    (dict(x=None), KVFP4_EINVAL), (dict(d=80), KVFP4_EUNSUPPORTED), (dict(codes=A16 + 2), KVFP4_EALIGN),
+    (dict(scales=A16 + 2), KVFP4_EALIGN),
+])
+def test_rtn_quantize_rejects(kw, want):
+    a = dict(x=A16, rows=10, d=128, bits=4, codes=A16, scales=A16)
+    a.update(kw)
+    assert lib.kvfp4_rtn_quantize(a["x"], a["rows"], a["d"], a["bits"], a["codes"], a["scales"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(bits=1), KVFP4_EINVAL), (dict(tail_rows=-1), KVFP4_EINVAL), (dict(tail=None), KVFP4_EINVAL),
+    (dict(y=None), KVFP4_EINVAL), (dict(tail=A16 + 8), KVFP4_EALIGN), (dict(d=16), KVFP4_EUNSUPPORTED),
+])
+def test_rtn_dequantize_rejects(kw, want):
+    a = dict(codes=A16, scales=A16, rows=10, d=128, bits=2, tail=A16, tail_rows=3, y=A16)
+    a.update(kw)
+    assert lib.kvfp4_rtn_dequantize(a["codes"], a["scales"], a["rows"], a["d"], a["bits"], a["tail"],
+                                    a["tail_rows"], a["y"], None) == want
+
+
+def test_rtn_zero_rows_is_a_noop():
+    assert lib.kvfp4_rtn_quantize(None, 0, 128, 4, None, None, None) == KVFP4_OK
+    assert lib.kvfp4_rtn_dequantize(None, None, 0, 128, 4, None, 0, None, None) == KVFP4_OK

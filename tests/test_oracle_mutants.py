@@ -11,7 +11,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvfp4_oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_attend.py")]
+             ("test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_attend.py",
+              "test_oracle_paged.py", "test_oracle_rtn.py")]
 
 MUTANTS = {
     "e2m1 ties to odd": ("(d == bestd && (c % 2) == 0)", "(d == bestd && (c % 2) == 1)"),
@@ -35,6 +36,14 @@ MUTANTS = {
                                    "float s_dec = A / (E2M1_MAX * E4M3_MAX * 2.0f);\n  int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int i = 0;"),
     "group amax from first row": ("for (int64_t i = 0; i < n; ++i) {\n    float v = fabsf", "for (int64_t i = 0; i < (n < 16 ? n : 16); ++i) {\n    float v = fabsf"),
     "attention scale ignored": ("s *= scale;", "s *= 1.0;"),
+    "paged uses block index as page": ("int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),",
+                                       "pg = b; int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),"),
+    "rtn truncates": ("float v = rintf(xb[i] * inv);", "float v = truncf(xb[i] * inv);"),
+    "rtn qmax off by one": ("const int qmax = (1 << (bits - 1)) - 1;\n  const int per_byte = 8 / bits;\n  const int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int b = 0;",
+                            "const int qmax = (1 << (bits - 1));\n  const int per_byte = 8 / bits;\n  const int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int b = 0;"),
+    "rtn scale kept in fp32": ("uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);\n      float sv = kvfp4_oracle_bf16_to_float(sh);",
+                               "uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);\n      float sv = m / (float)qmax;"),
+    "rtn dequant drops sign": ("int q = (raw >= (1 << (bits - 1))) ? raw - (1 << bits) : raw;", "int q = raw;"),
     "attention keys off by one": ("const uint16_t* kr = k + (j * heads + h) * d;",
                                   "const uint16_t* kr = k + (((j + 1) % tk) * heads + h) * d;"),
 }
