@@ -342,24 +342,48 @@ __global__ __launch_bounds__(kQuantThreads) void rtn_quant_kernel(const uint4* _
   }
 }
 
+// Sign-extend the eight BITS-wide fields of w, scale by the block scale and round to bf16.
+template <int BITS>
+__device__ __forceinline__ uint4 rtn_decode8(uint32_t w, uint32_t scale_bits) {
+  const float sv = __uint_as_float(scale_bits << 16);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = (int)(w << (32 - BITS * (i + 1))) >> (32 - BITS);  // sign-extend field i
+    f[i] = (float)q * sv;
+  }
+  uint4 o;
+  o.x = pack_bf16x2(f[0], f[1]);
+  o.y = pack_bf16x2(f[2], f[3]);
+  o.z = pack_bf16x2(f[4], f[5]);
+  o.w = pack_bf16x2(f[6], f[7]);
+  return o;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t rtn_word(const void* codes, int64_t u) {
+  return (BITS == 4) ? ((const uint32_t*)codes)[u] : (uint32_t)((const uint16_t*)codes)[u];
+}
+
 // Dequantize a packed prefix of `prefix_units` units, then copy a bf16 tail (the recent,
-// unquantized rows) behind it in the same launch.
+// unquantized rows) behind it in the same launch.  Workgroups that lie wholly in the prefix
+// or wholly in the tail load with indexes clamped into their own range, so every load is
+// unconditional and all of them are in flight before the first use; only the one workgroup
+// that straddles the boundary decides per lane.
 template <int BITS>
 __global__ __launch_bounds__(kDqThreads) void rtn_dequant_kernel(const void* __restrict__ codes,
                                                                  const uint16_t* __restrict__ scales,
                                                                  const uint4* __restrict__ tail,
                                                                  int64_t prefix_units,
                                                                  uint4* __restrict__ y, Part p) {
-  const Range r = wg_range(p);
+  const Range r = wg_range(p);  // never empty: one group, slices cover it
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t base = r.beg + wave * 64 * kDqUnroll;
-  if (r.beg >= prefix_units) {  // uniform: a workgroup of the bf16 tail only
+  if (r.beg >= prefix_units) {  // uniform: tail only
     uint4 t[kDqUnroll];
 #pragma unroll
-    for (int k = 0; k < kDqUnroll; ++k) {
-      const int64_t u = base + k * 64 + lane;
-      t[k] = u < r.end ? tail[u - prefix_units] : make_uint4(0, 0, 0, 0);
-    }
+    for (int k = 0; k < kDqUnroll; ++k)
+      t[k] = tail[min(base + k * 64 + lane, r.end - 1) - prefix_units];
 #pragma unroll
     for (int k = 0; k < kDqUnroll; ++k) {
       const int64_t u = base + k * 64 + lane;
@@ -367,35 +391,28 @@ __global__ __launch_bounds__(kDqThreads) void rtn_dequant_kernel(const void* __r
     }
     return;
   }
-  // Packed prefix (a workgroup may also hold the first tail units: handled per lane).
-  uint32_t w[kDqUnroll], sb[kDqUnroll];
+  if (r.end <= prefix_units) {  // uniform: packed prefix only
+    uint32_t w[kDqUnroll], sb[kDqUnroll];
 #pragma unroll
-  for (int k = 0; k < kDqUnroll; ++k) {
-    const int64_t u = base + k * 64 + lane;
-    const bool ok = u < r.end && u < prefix_units;
-    w[k] = ok ? ((BITS == 4) ? ((const uint32_t*)codes)[u] : (uint32_t)((const uint16_t*)codes)[u]) : 0u;
-    sb[k] = ok ? (uint32_t)scales[u >> 1] : 0u;
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t ui = min(base + k * 64 + lane, r.end - 1);
+      w[k] = rtn_word<BITS>(codes, ui);
+      sb[k] = scales[ui >> 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      if (u < r.end) store_nt(y + u, rtn_decode8<BITS>(w[k], sb[k]));
+    }
+    return;
   }
+  // The boundary workgroup.
 #pragma unroll
   for (int k = 0; k < kDqUnroll; ++k) {
     const int64_t u = base + k * 64 + lane;
     if (u >= r.end) continue;
-    uint4 o;
-    if (u < prefix_units) {
-      const float sv = __uint_as_float(sb[k] << 16);
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = (int)(w[k] << (32 - BITS * (i + 1))) >> (32 - BITS);  // sign-extend field i
-        f[i] = (float)q * sv;
-      }
-      o.x = pack_bf16x2(f[0], f[1]);
-      o.y = pack_bf16x2(f[2], f[3]);
-      o.z = pack_bf16x2(f[4], f[5]);
-      o.w = pack_bf16x2(f[6], f[7]);
-    } else {
-      o = tail[u - prefix_units];
-    }
+    const uint4 o = (u < prefix_units) ? rtn_decode8<BITS>(rtn_word<BITS>(codes, u), scales[u >> 1])
+                                       : tail[u - prefix_units];
     store_nt(y + u, o);
   }
 }
