@@ -46,6 +46,8 @@ def parse_args(argv=None):
                     help="skip the RTN INT4/INT2 timing (reported beside the step)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache gather timing (reported beside the step)")
+    ap.add_argument("--no-f32-fake", action="store_true",
+                    help="skip the float32-output dequantize and fake-quantize timings")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip the fused dequantize+attention timing (reported beside the step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -250,6 +252,53 @@ def cpu_baseline(cfg, rule, budget_s=12.0):
                        f"{done_dq} elements in {dt:.1f} s, single-threaded C oracle")}
 
 
+# ---- float32 output and fake quantization (on the step's own workload) ------------------------
+
+def _time_calls(fn, device, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream(device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize(device)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize(device)
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def bench_f32_fake(w, device, steps=20, warmup=3):
+    """(1) dequantize the whole packed cache to float32 (algorithmic bytes 0.5625 + 4 per
+    element + 4 per group); (2) fake-quantize the appended chunk of every layer's K and V
+    with the step's rule (bf16 in, bf16 out: 4 B per element + 4 per group)."""
+    import torch
+    y32 = torch.empty((w.rows, w.cfg.head_dim), dtype=torch.float32, device=device)
+    ms = _time_calls(lambda: w.kv.kvfp4_dequantize_f32(w.codes, w.scales, w.amax, w.rpg, y=y32),
+                     device, steps, warmup)
+    nb = w.cache_elems * (0.5 + 1.0 / 16.0 + 4.0) + 4 * w.n_groups
+    res = {"dequantize_f32": {"workload": f"{w.cfg.name}: whole cache to float32",
+                              "ms": round(ms, 4), "bytes": nb,
+                              "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                              "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}}
+    del y32
+    yf = torch.empty_like(w.append_src)
+    af = torch.empty((w.cfg.groups_per_chunk,), dtype=torch.float32, device=device)
+    ms = _time_calls(lambda: w.kv.kvfp4_fake_quantize(w.append_src, w.rpg, w.rule, y=yf,
+                                                      group_amax=af), device, steps, warmup)
+    nb = w.append_elems * 4.0 + 4 * w.cfg.groups_per_chunk
+    res["fake_quantize"] = {"workload": (f"{w.cfg.name}: one {w.cfg.chunk_tokens}-token chunk of "
+                                         f"every layer's K and V ({w.rule}), bf16 to bf16"),
+                            "ms": round(ms, 4), "bytes": nb,
+                            "GBps": round(nb / (ms * 1e-3) / 1e9, 2),
+                            "pct_of_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del yf, af
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---- fused dequantize + attention (its own workload) ---------------------------------------
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -408,6 +457,9 @@ def main(argv=None):
                       "append_bytes": w.append_bytes(),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
     }
+    if not args.no_f32_fake:
+        print("bench: timing float32 dequantize and fake quantize", file=sys.stderr, flush=True)
+        res.update(bench_f32_fake(w, dev))
     if not args.no_rtn:
         print("bench: timing the RTN INT4/INT2 caches", file=sys.stderr, flush=True)
         res["rtn"] = bench_rtn(dev)

@@ -167,6 +167,36 @@ int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scales, const fl
                            int32_t head_dim, int64_t n_pages, uint16_t* y, void* stream);
 
 /*
+ * Float32 output and fake quantization.  [P-NVFP4] "Stage 3" (the dequantize kernel emits
+ * float32 or bf16) and "Stage 1" (the fake-quant form of the block-scale path, where a
+ * 16-bit tensor carries exactly the values the 4-bit one represents).
+ *
+ * kvfp4_dequantize_f32 / kvfp4_dequantize_paged_f32: as kvfp4_dequantize /
+ * kvfp4_dequantize_paged, but y receives the binary32 products E2M1(c) * S with
+ * S = E4M3(sf) * (A/2688) -- the values whose bf16 rounding the bf16 calls return.
+ *   y (out) float [rows, head_dim] (paged: [n_blocks * rows_per_page, head_dim]); 16-byte
+ *           aligned.
+ *
+ * kvfp4_fake_quantize: quantize x exactly as kvfp4_quantize does (same rule, groups and
+ * group_amax output) and write dequantize(quantize(x)) in bf16 to y, bit-identical to
+ * calling the two, without storing codes or scale bytes.
+ *   x, rows, head_dim, rows_per_group, rule   as for kvfp4_quantize
+ *   group_amax (out) float [ceil(rows/rows_per_group)]; 4-byte aligned
+ *   y (out)    bf16 [rows, head_dim]; 16-byte aligned; y == x (in place) is allowed, any
+ *              other overlap is undefined.
+ * Errors, alignment and stream rules as for the calls above.
+ */
+int kvfp4_dequantize_f32(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
+                         int64_t rows, int32_t head_dim, int64_t rows_per_group, float* y,
+                         void* stream);
+int kvfp4_dequantize_paged_f32(const uint8_t* codes, const uint8_t* scales,
+                               const float* page_amax, const int32_t* block_table,
+                               int64_t n_blocks, int64_t rows_per_page, int32_t head_dim,
+                               int64_t n_pages, float* y, void* stream);
+int kvfp4_fake_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
+                        int32_t rule, float* group_amax, uint16_t* y, void* stream);
+
+/*
  * Round-to-nearest symmetric blockwise integer quantization (INT4 or INT2) -- the RTN
  * baselines of [P-SF] Table 3: RTN_INT4, RTN_INT2, RTN_K2_V4 (2-bit keys, 4-bit values: two
  * calls with different `bits`) and RTN_INT4 RECENT2 (the newest frame-blocks stay bf16 and

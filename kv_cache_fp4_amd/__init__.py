@@ -39,6 +39,12 @@ def _load() -> ctypes.CDLL:
     L.kvfp4_quantize_paged.restype = ctypes.c_int
     L.kvfp4_dequantize_paged.argtypes = [P, P, P, P, i64, i64, i32, i64, P, P]
     L.kvfp4_dequantize_paged.restype = ctypes.c_int
+    L.kvfp4_dequantize_f32.argtypes = [P, P, P, i64, i32, i64, P, P]
+    L.kvfp4_dequantize_f32.restype = ctypes.c_int
+    L.kvfp4_dequantize_paged_f32.argtypes = [P, P, P, P, i64, i64, i32, i64, P, P]
+    L.kvfp4_dequantize_paged_f32.restype = ctypes.c_int
+    L.kvfp4_fake_quantize.argtypes = [P, i64, i32, i64, i32, P, P, P]
+    L.kvfp4_fake_quantize.restype = ctypes.c_int
     L.kvfp4_rtn_quantize.argtypes = [P, i64, i32, i32, P, P, P]
     L.kvfp4_rtn_quantize.restype = ctypes.c_int
     L.kvfp4_rtn_dequantize.argtypes = [P, P, i64, i32, i32, P, i64, P, P]
@@ -135,6 +141,36 @@ def kvfp4_dequantize(codes, scales, group_amax, rows_per_group: int, y=None, str
     return y
 
 
+def kvfp4_dequantize_f32(codes, scales, group_amax, rows_per_group: int, y=None, stream=None):
+    """Dequantize a packed tensor to float32 [rows, head_dim] (the products before bf16
+    rounding; written into ``y`` if given)."""
+    import torch
+    rows = codes.shape[0]
+    head_dim = codes.shape[1] * 2 if codes.dim() == 2 else 0
+    if y is None:
+        y = torch.empty((rows, head_dim), dtype=torch.float32, device=codes.device)
+    _check(lib.kvfp4_dequantize_f32(_ptr(codes), _ptr(scales), _ptr(group_amax), rows, head_dim,
+                                    rows_per_group, _ptr(y), _stream(stream, codes.device)))
+    return y
+
+
+def kvfp4_fake_quantize(x, rows_per_group: int, rule="static_6", y=None, group_amax=None,
+                        stream=None):
+    """bf16 ``x`` [..., head_dim] -> (dequantize(quantize(x)) as bf16 [rows, head_dim],
+    group_amax float32 [n_groups]) without a packed copy.  ``y`` may be ``x`` (in place)."""
+    import torch
+    head_dim = x.shape[-1]
+    rows = x.numel() // head_dim if head_dim else 0
+    _, _, ng = kvfp4_packed_sizes(rows, head_dim, rows_per_group)
+    if y is None:
+        y = torch.empty((rows, head_dim), dtype=torch.bfloat16, device=x.device)
+    if group_amax is None:
+        group_amax = torch.empty((ng,), dtype=torch.float32, device=x.device)
+    _check(lib.kvfp4_fake_quantize(_ptr(x), rows, head_dim, rows_per_group, _rule(rule),
+                                   _ptr(group_amax), _ptr(y), _stream(stream, x.device)))
+    return y, group_amax
+
+
 def kvfp4_quantize_paged(x, block_table, rows_per_page: int, codes, scales, page_amax,
                          rule="static_6", stream=None):
     """Quantize dense bf16 rows ``x`` [n_blocks*rows_per_page, head_dim] into the pages of a
@@ -163,6 +199,22 @@ def kvfp4_dequantize_paged(codes, scales, page_amax, block_table, rows_per_page:
     _check(lib.kvfp4_dequantize_paged(_ptr(codes), _ptr(scales), _ptr(page_amax),
                                       _ptr(block_table), n_blocks, rows_per_page, head_dim,
                                       n_pages, _ptr(y), _stream(stream, codes.device)))
+    return y
+
+
+def kvfp4_dequantize_paged_f32(codes, scales, page_amax, block_table, rows_per_page: int,
+                               y=None, stream=None):
+    """As kvfp4_dequantize_paged, with float32 output."""
+    import torch
+    head_dim = codes.shape[-1] * 2
+    n_blocks = block_table.numel()
+    n_pages = page_amax.numel()
+    if y is None:
+        y = torch.empty((n_blocks * rows_per_page, head_dim), dtype=torch.float32,
+                        device=codes.device)
+    _check(lib.kvfp4_dequantize_paged_f32(_ptr(codes), _ptr(scales), _ptr(page_amax),
+                                          _ptr(block_table), n_blocks, rows_per_page, head_dim,
+                                          n_pages, _ptr(y), _stream(stream, codes.device)))
     return y
 
 
@@ -216,5 +268,7 @@ def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
     return out
 
 
-__all__ = ["kvfp4_rtn_quantize", "kvfp4_rtn_dequantize", "kvfp4_attend", "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_quantize", "kvfp4_dequantize", "kvfp4_packed_sizes", "KVFP4Error", "RULES",
-           "lib", "LIB_PATH"]
+__all__ = ["kvfp4_quantize", "kvfp4_dequantize", "kvfp4_dequantize_f32", "kvfp4_fake_quantize",
+           "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_dequantize_paged_f32",
+           "kvfp4_rtn_quantize", "kvfp4_rtn_dequantize", "kvfp4_attend", "kvfp4_packed_sizes",
+           "KVFP4Error", "RULES", "lib", "LIB_PATH"]

@@ -216,11 +216,17 @@ __device__ __forceinline__ float half_err(const float xf[8], const Cand& c) {
   return e;
 }
 
-template <int RULE, int THREADS, int UNR>
-__global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict__ x,
+// FAKE: instead of storing codes and scale bytes, store the block dequantized to bf16
+// (decode8 with the chosen candidate's S, which is E4M3(sf) * s_dec exactly as the
+// dequantize kernel computes it), so the output equals dequantize(quantize(x)).
+// x and fake_y are not restrict: fake quantization may run in place (each lane reads its
+// unit before it writes the same unit, and no other lane touches it).
+template <int RULE, int THREADS, int UNR, bool FAKE>
+__global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* x,
                                                         const float* __restrict__ amax,
                                                         uint32_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, Part p) {
+                                                        uint8_t* __restrict__ scales,
+                                                        uint4* fake_y, Part p) {
   const Range r = wg_range(p);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (r.beg >= r.end) return;  // uniform: skipped page or empty slice
@@ -260,9 +266,13 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* __restrict_
         pick = (err4 < err6) ? c4 : c6;
       }
       if (u < r.end) {
-        const int64_t pu = u + r.shift;
-        __builtin_nontemporal_store(pick.codes, codes + pu);
-        if ((lane & 1) == 0) scales[pu >> 1] = (uint8_t)pick.sf;
+        if constexpr (FAKE) {
+          store_nt(fake_y + u, decode8(pick.codes, pick.S));
+        } else {
+          const int64_t pu = u + r.shift;
+          __builtin_nontemporal_store(pick.codes, codes + pu);
+          if ((lane & 1) == 0) scales[pu >> 1] = (uint8_t)pick.sf;
+        }
       }
     }
   }
@@ -292,6 +302,45 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
   for (int k = 0; k < kDqUnroll; ++k) {
     const int64_t u = base + k * 64 + lane;
     if (u < r.end) store_nt(y + u, decode8(c[k], e4m3_decode(sf[k]) * s_dec));
+  }
+}
+
+// float32 output ([P-NVFP4] "Stage 3": float32 or bf16).  A lane takes half a unit (4
+// elements: one 16-bit code load, one 16 B store), so each wave store still covers one
+// contiguous 1 KiB span; the slice is the same 256 units as the bf16 kernel.
+constexpr int kDqfThreads = 128, kDqfUnroll = 4;  // half units per lane
+static_assert(kDqfThreads * kDqfUnroll == 2 * kDqThreads * kDqUnroll, "same slice as bf16");
+
+__global__ __launch_bounds__(kDqfThreads) void dequant_f32_kernel(const uint16_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const float* __restrict__ amax,
+                                                                  float4* __restrict__ y, Part p) {
+  const Range r = wg_range(p);
+  if (r.beg >= r.end) return;  // uniform: skipped page or empty slice
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float s_dec = amax[r.page] / kGlobalDiv;
+  const int64_t he = 2 * r.end, hs = 2 * r.shift;  // half units
+  const int64_t base = 2 * r.beg + wave * 64 * kDqfUnroll;
+  uint32_t c[kDqfUnroll], sf[kDqfUnroll];
+#pragma unroll
+  for (int k = 0; k < kDqfUnroll; ++k) {
+    const int64_t h = min(base + k * 64 + lane, he - 1) + hs;  // clamped: always in range
+    c[k] = codes[h];
+    sf[k] = scales[h >> 2];
+  }
+#pragma unroll
+  for (int k = 0; k < kDqfUnroll; ++k) {
+    const int64_t h = base + k * 64 + lane;
+    if (h < he) {
+      const float S = e4m3_decode(sf[k]) * s_dec;
+      const f32x2 a = e2m1_decode2<0>(c[k]), b = e2m1_decode2<1>(c[k]);
+      float4 o;
+      o.x = a.x * S;
+      o.y = a.y * S;
+      o.z = b.x * S;
+      o.w = b.y * S;
+      store_nt((uint4*)(y + h), __builtin_bit_cast(uint4, o));
+    }
   }
 }
 
@@ -465,22 +514,27 @@ int launched() {
 template <int RULE, int THREADS, int UNR, int STEPS>
 int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
                  const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
-                 const float* amax, hipStream_t s) {
+                 const float* amax, uint16_t* fake_y, hipStream_t s) {
   Part part;
   unsigned grid = 0;
   int rc = plan(rows, head_dim, rpg, tile_units(THREADS, UNR, STEPS), &part, &grid);
   if (rc != KVFP4_OK) return rc;
   part.table = table;
   if (table) part.n_pages = n_pages;
-  hipLaunchKernelGGL((quant_kernel<RULE, THREADS, UNR>), dim3(grid), dim3(THREADS), 0, s,
-                     (const uint4*)x, amax, (uint32_t*)codes, scales, part);
+  if (fake_y)
+    hipLaunchKernelGGL((quant_kernel<RULE, THREADS, UNR, true>), dim3(grid), dim3(THREADS), 0, s,
+                       (const uint4*)x, amax, nullptr, nullptr, (uint4*)fake_y, part);
+  else
+    hipLaunchKernelGGL((quant_kernel<RULE, THREADS, UNR, false>), dim3(grid), dim3(THREADS), 0,
+                       s, (const uint4*)x, amax, (uint32_t*)codes, scales, nullptr, part);
   return launched();
 }
 
-// Shared body of the dense and paged quantize entry points (arguments already checked).
+// Shared body of the dense, paged and fake quantize entry points (arguments already
+// checked).  With fake_y set, the encode pass writes bf16 there instead of codes/scales.
 int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
-                  float* group_amax, hipStream_t s) {
+                  float* group_amax, uint16_t* fake_y, hipStream_t s) {
   Part apart;
   unsigned agrid = 0;
   int rc = plan(rows, head_dim, rpg, tile_units(kAmaxThreads, kAmaxUnroll, kAmaxSteps), &apart,
@@ -500,27 +554,32 @@ int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
   switch (rule) {
     case KVFP4_RULE_STATIC6:
       return launch_quant<KVFP4_RULE_STATIC6, kQuantThreads, kQuantUnroll, kQuantSteps>(
-          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s);
     case KVFP4_RULE_STATIC4:
       return launch_quant<KVFP4_RULE_STATIC4, kQuantThreads, kQuantUnroll, kQuantSteps>(
-          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s);
     default:
       return launch_quant<KVFP4_RULE_MSE, kMseThreads, kMseUnroll, kMseSteps>(
-          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, s);
+          x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s);
   }
 }
 
+// Shared body of the dequantize entry points: bf16 output to y16, or float32 to y32.
 int dequantize_impl(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
                     int64_t rows, int32_t head_dim, int64_t rpg, const int32_t* table,
-                    int64_t n_pages, uint16_t* y, hipStream_t s) {
+                    int64_t n_pages, uint16_t* y16, float* y32, hipStream_t s) {
   Part part;
   unsigned grid = 0;
   int rc = plan(rows, head_dim, rpg, tile_units(kDqThreads, kDqUnroll, 1), &part, &grid);
   if (rc != KVFP4_OK) return rc;
   part.table = table;
   if (table) part.n_pages = n_pages;
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, s, (const uint32_t*)codes,
-                     scales, group_amax, (uint4*)y, part);
+  if (y32)
+    hipLaunchKernelGGL(dequant_f32_kernel, dim3(grid), dim3(kDqfThreads), 0, s,
+                       (const uint16_t*)codes, scales, group_amax, (float4*)y32, part);
+  else
+    hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, s,
+                       (const uint32_t*)codes, scales, group_amax, (uint4*)y16, part);
   return launched();
 }
 
@@ -549,21 +608,52 @@ extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4))
     return KVFP4_EALIGN;
   return quantize_impl(x, rows, head_dim, rows_per_group, rule, nullptr, 0, codes, scales,
-                       group_amax, (hipStream_t)stream);
+                       group_amax, nullptr, (hipStream_t)stream);
+}
+
+static int dequantize_entry(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
+                            int64_t rows, int32_t head_dim, int64_t rows_per_group, uint16_t* y16,
+                            float* y32, void* stream) {
+  int64_t ng = 0;
+  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
+  if (rc != KVFP4_OK) return rc;
+  if (rows == 0) return KVFP4_OK;
+  const void* y = y32 ? (const void*)y32 : (const void*)y16;
+  if (!codes || !scales || !group_amax || !y) return KVFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4) || !aligned(y, 16))
+    return KVFP4_EALIGN;
+  return dequantize_impl(codes, scales, group_amax, rows, head_dim, rows_per_group, nullptr, 0,
+                         y16, y32, (hipStream_t)stream);
 }
 
 extern "C" int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                                 const float* group_amax, int64_t rows, int32_t head_dim,
                                 int64_t rows_per_group, uint16_t* y, void* stream) {
+  return dequantize_entry(codes, scales, group_amax, rows, head_dim, rows_per_group, y, nullptr,
+                          stream);
+}
+
+extern "C" int kvfp4_dequantize_f32(const uint8_t* codes, const uint8_t* scales,
+                                    const float* group_amax, int64_t rows, int32_t head_dim,
+                                    int64_t rows_per_group, float* y, void* stream) {
+  if (rows > 0 && !y) return KVFP4_EINVAL;  // a null y would otherwise select bf16 output
+  return dequantize_entry(codes, scales, group_amax, rows, head_dim, rows_per_group, nullptr, y,
+                          stream);
+}
+
+extern "C" int kvfp4_fake_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
+                                   int64_t rows_per_group, int32_t rule, float* group_amax,
+                                   uint16_t* y, void* stream) {
+  if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
+    return KVFP4_EINVAL;
   int64_t ng = 0;
   int rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
-  if (!codes || !scales || !group_amax || !y) return KVFP4_EINVAL;
-  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4) || !aligned(y, 16))
-    return KVFP4_EALIGN;
-  return dequantize_impl(codes, scales, group_amax, rows, head_dim, rows_per_group, nullptr, 0, y,
-                         (hipStream_t)stream);
+  if (!x || !group_amax || !y) return KVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(group_amax, 4)) return KVFP4_EALIGN;
+  return quantize_impl(x, rows, head_dim, rows_per_group, rule, nullptr, 0, nullptr, nullptr,
+                       group_amax, y, (hipStream_t)stream);
 }
 
 // Paged cache: shared checks of the two paged entry points.
@@ -592,21 +682,40 @@ extern "C" int kvfp4_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4))
     return KVFP4_EALIGN;
   return quantize_impl(x, n_blocks * rows_per_page, head_dim, rows_per_page, rule, block_table,
-                       n_pages, codes, scales, page_amax, (hipStream_t)stream);
+                       n_pages, codes, scales, page_amax, nullptr, (hipStream_t)stream);
+}
+
+static int dequantize_paged_entry(const uint8_t* codes, const uint8_t* scales,
+                                  const float* page_amax, const int32_t* block_table,
+                                  int64_t n_blocks, int64_t rows_per_page, int32_t head_dim,
+                                  int64_t n_pages, uint16_t* y16, float* y32, void* stream) {
+  int rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
+  if (rc != KVFP4_OK) return rc;
+  if (n_blocks == 0) return KVFP4_OK;
+  const void* y = y32 ? (const void*)y32 : (const void*)y16;
+  if (!codes || !scales || !page_amax || !y) return KVFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4) || !aligned(y, 16))
+    return KVFP4_EALIGN;
+  return dequantize_impl(codes, scales, page_amax, n_blocks * rows_per_page, head_dim,
+                         rows_per_page, block_table, n_pages, y16, y32, (hipStream_t)stream);
 }
 
 extern "C" int kvfp4_dequantize_paged(const uint8_t* codes, const uint8_t* scales,
                                       const float* page_amax, const int32_t* block_table,
                                       int64_t n_blocks, int64_t rows_per_page, int32_t head_dim,
                                       int64_t n_pages, uint16_t* y, void* stream) {
-  int rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
-  if (rc != KVFP4_OK) return rc;
-  if (n_blocks == 0) return KVFP4_OK;
-  if (!codes || !scales || !page_amax || !y) return KVFP4_EINVAL;
-  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4) || !aligned(y, 16))
-    return KVFP4_EALIGN;
-  return dequantize_impl(codes, scales, page_amax, n_blocks * rows_per_page, head_dim,
-                         rows_per_page, block_table, n_pages, y, (hipStream_t)stream);
+  return dequantize_paged_entry(codes, scales, page_amax, block_table, n_blocks, rows_per_page,
+                                head_dim, n_pages, y, nullptr, stream);
+}
+
+extern "C" int kvfp4_dequantize_paged_f32(const uint8_t* codes, const uint8_t* scales,
+                                          const float* page_amax, const int32_t* block_table,
+                                          int64_t n_blocks, int64_t rows_per_page,
+                                          int32_t head_dim, int64_t n_pages, float* y,
+                                          void* stream) {
+  if (n_blocks > 0 && !y) return KVFP4_EINVAL;  // a null y would otherwise select bf16 output
+  return dequantize_paged_entry(codes, scales, page_amax, block_table, n_blocks, rows_per_page,
+                                head_dim, n_pages, nullptr, y, stream);
 }
 
 extern "C" int kvfp4_rtn_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int32_t bits,

@@ -68,6 +68,14 @@ def lib() -> ctypes.CDLL:
         L.kvfp4_oracle_dequantize_rows.restype = i32
         L.kvfp4_oracle_dequantize.argtypes = [P, P, P, i64, i32, i64, P]
         L.kvfp4_oracle_dequantize.restype = i32
+        L.kvfp4_oracle_dequantize_rows_f32.argtypes = [P, P, i64, i32, f32, P]
+        L.kvfp4_oracle_dequantize_rows_f32.restype = i32
+        L.kvfp4_oracle_dequantize_f32.argtypes = [P, P, P, i64, i32, i64, P]
+        L.kvfp4_oracle_dequantize_f32.restype = i32
+        L.kvfp4_oracle_dequantize_paged_f32.argtypes = [P, P, P, P, i64, i64, i32, i64, P]
+        L.kvfp4_oracle_dequantize_paged_f32.restype = i32
+        L.kvfp4_oracle_fake_quantize.argtypes = [P, i64, i32, i64, i32, P, P]
+        L.kvfp4_oracle_fake_quantize.restype = i32
         L.kvfp4_oracle_attend_rows.argtypes = [P, P, P, i64, i32, i32, f64, P, i64, P, P]
         L.kvfp4_oracle_attend_rows.restype = i32
         L.kvfp4_oracle_quantize_paged.argtypes = [P, i64, i64, i32, i32, P, i64, P, P, P]
@@ -183,6 +191,49 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, amax: np.ndarray,
     return y
 
 
+def dequantize_f32(codes: np.ndarray, scales: np.ndarray, amax: np.ndarray,
+                   rows_per_group: int) -> np.ndarray:
+    """Float32 output: the binary32 products before the bf16 rounding."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    rows, half = codes.shape
+    d = half * 2
+    y = np.zeros((rows, d), dtype=np.float32)
+    rc = lib().kvfp4_oracle_dequantize_f32(_p(codes), _p(scales), _p(amax), rows, d,
+                                           rows_per_group, _p(y))
+    if rc:
+        raise ValueError("oracle dequantize_f32: bad arguments")
+    return y
+
+
+def dequantize_rows_f32(codes: np.ndarray, scales: np.ndarray, amax: float) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, half = codes.shape
+    d = half * 2
+    y = np.zeros((rows, d), dtype=np.float32)
+    rc = lib().kvfp4_oracle_dequantize_rows_f32(_p(codes), _p(scales), rows, d, float(amax),
+                                                _p(y))
+    if rc:
+        raise ValueError("oracle dequantize_rows_f32: bad arguments")
+    return y
+
+
+def fake_quantize(x_bf16: np.ndarray, rows_per_group: int, rule="static_6"):
+    """Quantize then dequantize to bf16: (y u16 [rows, d], group_amax f32 [groups])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, d = x.shape
+    ng = (rows + rows_per_group - 1) // rows_per_group
+    y = np.zeros((rows, d), dtype=np.uint16)
+    amax = np.zeros(ng, dtype=np.float32)
+    rc = lib().kvfp4_oracle_fake_quantize(_p(x), rows, d, rows_per_group, _rule(rule), _p(amax),
+                                          _p(y))
+    if rc:
+        raise ValueError("oracle fake_quantize: bad arguments")
+    return y, amax
+
+
 def dequantize_rows(codes: np.ndarray, scales: np.ndarray, amax: float) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
@@ -228,6 +279,22 @@ def dequantize_paged(codes, scales, page_amax, table, rows_per_page: int, y=None
                                              table.size, rows_per_page, d, page_amax.size, _p(y))
     if rc:
         raise ValueError("oracle dequantize_paged: bad arguments")
+    return y
+
+
+def dequantize_paged_f32(codes, scales, page_amax, table, rows_per_page: int, y=None):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    page_amax = np.ascontiguousarray(page_amax, dtype=np.float32)
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    d = codes.shape[-1] * 2
+    if y is None:
+        y = np.zeros((table.size * rows_per_page, d), np.float32)
+    rc = lib().kvfp4_oracle_dequantize_paged_f32(_p(codes), _p(scales), _p(page_amax),
+                                                 _p(table), table.size, rows_per_page, d,
+                                                 page_amax.size, _p(y))
+    if rc:
+        raise ValueError("oracle dequantize_paged_f32: bad arguments")
     return y
 
 

@@ -34,6 +34,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------------------
@@ -248,25 +249,36 @@ int kvfp4_oracle_quantize(const uint16_t* x, int64_t rows, int d, int64_t rows_p
 
 /* ------------------------------------------------------------------------------------
  * Dequantization.  [P-NVFP4] "Stage 3" (each byte expands to two 4-bit values, which are
- * multiplied by the per-block and the global scale; bf16 output); [P-KV] "CUDA
- * De-quantization Pipeline" (bf16 reconstruction before attention).
- * out = bf16( E2M1(c) * S ),  S = E4M3(sf) * (A / 2688), each product rounded to binary32.
+ * multiplied by the per-block and the global scale; the output is float32 or bf16); [P-KV]
+ * "CUDA De-quantization Pipeline" (bf16 reconstruction before attention).
+ * v = E2M1(c) * S,  S = E4M3(sf) * (A / 2688), each product rounded to binary32;
+ * the float32 output is v itself, the bf16 output is v rounded to bf16.
  * ---------------------------------------------------------------------------------- */
+static float dequant_value(const uint8_t* codes, const uint8_t* scales, int64_t r, int d, int i,
+                           float s_dec) {
+  int nb = d / 16;
+  float S = (float)kvfp4_oracle_e4m3_value(scales[r * nb + i / 16]) * s_dec;
+  uint8_t byte = codes[r * (d / 2) + i / 2];
+  int c = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+  return (float)kvfp4_oracle_e2m1_value(c) * S;
+}
+
 int kvfp4_oracle_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                  int d, float A, uint16_t* y) {
   if (rows < 0 || d <= 0 || d % 16 != 0) return 1;
   float s_dec = A / (E2M1_MAX * E4M3_MAX);
-  int nb = d / 16;
-  for (int64_t r = 0; r < rows; ++r) {
-    for (int i = 0; i < d; ++i) {
-      int b = i / 16;
-      float S = (float)kvfp4_oracle_e4m3_value(scales[r * nb + b]) * s_dec;
-      uint8_t byte = codes[r * (d / 2) + i / 2];
-      int c = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
-      float v = (float)kvfp4_oracle_e2m1_value(c);
-      y[r * d + i] = kvfp4_oracle_float_to_bf16(v * S);
-    }
-  }
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < d; ++i)
+      y[r * d + i] = kvfp4_oracle_float_to_bf16(dequant_value(codes, scales, r, d, i, s_dec));
+  return 0;
+}
+
+int kvfp4_oracle_dequantize_rows_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                     int d, float A, float* y) {
+  if (rows < 0 || d <= 0 || d % 16 != 0) return 1;
+  float s_dec = A / (E2M1_MAX * E4M3_MAX);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < d; ++i) y[r * d + i] = dequant_value(codes, scales, r, d, i, s_dec);
   return 0;
 }
 
@@ -281,6 +293,37 @@ int kvfp4_oracle_dequantize(const uint8_t* codes, const uint8_t* scales,
     if (rc) return rc;
   }
   return 0;
+}
+
+int kvfp4_oracle_dequantize_f32(const uint8_t* codes, const uint8_t* scales,
+                                const float* group_amax, int64_t rows, int d,
+                                int64_t rows_per_group, float* y) {
+  if (rows < 0 || rows_per_group <= 0 || d <= 0 || d % 16 != 0) return 1;
+  for (int64_t r0 = 0, g = 0; r0 < rows; r0 += rows_per_group, ++g) {
+    int64_t n = (rows - r0 < rows_per_group) ? rows - r0 : rows_per_group;
+    int rc = kvfp4_oracle_dequantize_rows_f32(codes + r0 * (d / 2), scales + r0 * (d / 16), n,
+                                              d, group_amax[g], y + r0 * d);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+/* Fake quantization: the tensor as the cache would return it, i.e. quantize (every step
+ * above) and dequantize to bf16, without keeping the packed form.  [P-NVFP4] "Stage 1"
+ * (the fake-quant variant of the static block-scale path, used where a 16-bit tensor
+ * stands in for the 4-bit one).  Also returns each group's amax. */
+int kvfp4_oracle_fake_quantize(const uint16_t* x, int64_t rows, int d, int64_t rows_per_group,
+                               int rule, float* group_amax, uint16_t* y) {
+  if (rows < 0 || rows_per_group <= 0 || d <= 0 || d % 16 != 0) return 1;
+  if (rows == 0) return 0;
+  uint8_t* codes = (uint8_t*)malloc((size_t)(rows * (d / 2)));
+  uint8_t* scales = (uint8_t*)malloc((size_t)(rows * (d / 16)));
+  int rc = (codes && scales) ? 0 : 2;
+  if (!rc) rc = kvfp4_oracle_quantize(x, rows, d, rows_per_group, rule, codes, scales, group_amax);
+  if (!rc) rc = kvfp4_oracle_dequantize(codes, scales, group_amax, rows, d, rows_per_group, y);
+  free(codes);
+  free(scales);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------------------
@@ -317,6 +360,23 @@ int kvfp4_oracle_dequantize_paged(const uint8_t* codes, const uint8_t* scales,
     int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),
                                           scales + pg * rows_per_page * (d / 16), rows_per_page,
                                           d, page_amax[pg], y + b * rows_per_page * d);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int kvfp4_oracle_dequantize_paged_f32(const uint8_t* codes, const uint8_t* scales,
+                                      const float* page_amax, const int32_t* table,
+                                      int64_t n_blocks, int64_t rows_per_page, int d,
+                                      int64_t n_pages, float* y) {
+  if (n_blocks < 0 || rows_per_page <= 0 || d <= 0 || d % 16 != 0) return 1;
+  for (int64_t b = 0; b < n_blocks; ++b) {
+    int64_t pg = table[b];
+    if (pg < 0 || pg >= n_pages) continue;
+    int rc = kvfp4_oracle_dequantize_rows_f32(codes + pg * rows_per_page * (d / 2),
+                                              scales + pg * rows_per_page * (d / 16),
+                                              rows_per_page, d, page_amax[pg],
+                                              y + b * rows_per_page * d);
     if (rc) return rc;
   }
   return 0;

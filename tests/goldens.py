@@ -36,6 +36,9 @@ def load(name):
             "scales": np.array([int(t, 16) for t in s["scales"].split()], dtype=np.uint8),
             "codes": np.array([int(t, 16) for t in s["codes"].split()], dtype=np.uint8),
             "dequant": np.array([int(t, 16) for t in s["dequant_bf16"].split()], dtype=np.uint16),
+            # optional: the float32 dequant output as binary32 bit patterns
+            "dequant_f32": (np.array([int(t, 16) for t in s["dequant_f32"].split()],
+                                     dtype=np.uint32) if "dequant_f32" in s else None),
         })
     return out
 

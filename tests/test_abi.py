@@ -192,3 +192,51 @@ def test_rtn_dequantize_rejects(kw, want):
 def test_rtn_zero_rows_is_a_noop():
     assert lib.kvfp4_rtn_quantize(None, 0, 128, 4, None, None, None) == KVFP4_OK
     assert lib.kvfp4_rtn_dequantize(None, None, 0, 128, 4, None, 0, None, None) == KVFP4_OK
+
+
+def dqf(codes=A16, scales=A16, amax=A16, rows=64, d=128, rpg=64, y=A16):
+    return lib.kvfp4_dequantize_f32(codes, scales, amax, rows, d, rpg, y, None)
+
+
+def dqpf(codes=A16, scales=A16, amax=A16, tab=A16, nb=4, rpp=24, d=128, npg=8, y=A16):
+    return lib.kvfp4_dequantize_paged_f32(codes, scales, amax, tab, nb, rpp, d, npg, y, None)
+
+
+def fq(x=A16, rows=64, d=128, rpg=64, rule=0, amax=A16, y=A16):
+    return lib.kvfp4_fake_quantize(x, rows, d, rpg, rule, amax, y, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-3), KVFP4_EINVAL), (dict(rpg=0), KVFP4_EINVAL), (dict(codes=None), KVFP4_EINVAL),
+    (dict(amax=None), KVFP4_EINVAL), (dict(y=None), KVFP4_EINVAL), (dict(d=16), KVFP4_EUNSUPPORTED),
+    (dict(y=A16 + 4), KVFP4_EALIGN), (dict(codes=A16 + 1), KVFP4_EALIGN),
+    (dict(scales=A16 + 1), KVFP4_EALIGN),
+])
+def test_dequantize_f32_rejects(kw, want):
+    assert dqf(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=-1), KVFP4_EINVAL), (dict(tab=None), KVFP4_EINVAL), (dict(y=None), KVFP4_EINVAL),
+    (dict(d=32), KVFP4_EUNSUPPORTED), (dict(y=A16 + 8), KVFP4_EALIGN),
+    (dict(amax=A16 + 2), KVFP4_EALIGN),
+])
+def test_dequantize_paged_f32_rejects(kw, want):
+    assert dqpf(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), KVFP4_EINVAL), (dict(rpg=0), KVFP4_EINVAL), (dict(rule=3), KVFP4_EINVAL),
+    (dict(x=None), KVFP4_EINVAL), (dict(amax=None), KVFP4_EINVAL), (dict(y=None), KVFP4_EINVAL),
+    (dict(d=96), KVFP4_EUNSUPPORTED), (dict(x=A16 + 8), KVFP4_EALIGN),
+    (dict(y=A16 + 2), KVFP4_EALIGN), (dict(amax=A16 + 2), KVFP4_EALIGN),
+    (dict(rows=1 << 50), KVFP4_EINVAL),
+])
+def test_fake_quantize_rejects(kw, want):
+    assert fq(**kw) == want
+
+
+def test_f32_and_fake_zero_rows_are_noops():
+    assert dqf(rows=0, codes=None, scales=None, amax=None, y=None) == KVFP4_OK
+    assert dqpf(nb=0, codes=None, scales=None, amax=None, tab=None, y=None) == KVFP4_OK
+    assert fq(rows=0, x=None, amax=None, y=None) == KVFP4_OK

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvfp4_oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", f) for f in
              ("test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_attend.py",
-              "test_oracle_paged.py", "test_oracle_rtn.py")]
+              "test_oracle_paged.py", "test_oracle_rtn.py", "test_oracle_f32_fake.py")]
 
 MUTANTS = {
     "e2m1 ties to odd": ("(d == bestd && (c % 2) == 0)", "(d == bestd && (c % 2) == 1)"),
@@ -32,8 +32,14 @@ MUTANTS = {
     "mse error not squared": ("e_lo = fmaf(d, d, e_lo);", "e_lo = fmaf(fabsf(d), 1.0f, e_lo);"),
     "reciprocal perturbed": ("float inv = (S > 0.0f) ? 1.0f / S : 0.0f;",
                              "float inv = (S > 0.0f) ? 1.0f / (S * 1.0001f) : 0.0f;"),
-    "dequant drops global scale": ("float s_dec = A / (E2M1_MAX * E4M3_MAX);\n  int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int i = 0;",
-                                   "float s_dec = A / (E2M1_MAX * E4M3_MAX * 2.0f);\n  int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int i = 0;"),
+    "dequant drops global scale": ("float S = (float)kvfp4_oracle_e4m3_value(scales[r * nb + i / 16]) * s_dec;",
+                                   "float S = (float)kvfp4_oracle_e4m3_value(scales[r * nb + i / 16]) * s_dec * 2.0f;"),
+    "dequant product order": ("return (float)kvfp4_oracle_e2m1_value(c) * S;",
+                              "return (float)((float)kvfp4_oracle_e2m1_value(c) * (float)kvfp4_oracle_e4m3_value(scales[r * nb + i / 16])) * s_dec; (void)S;"),
+    "fake quant ignores the rule": ("if (!rc) rc = kvfp4_oracle_quantize(x, rows, d, rows_per_group, rule, codes, scales, group_amax);",
+                                    "if (!rc) rc = kvfp4_oracle_quantize(x, rows, d, rows_per_group, 0, codes, scales, group_amax);"),
+    "paged f32 uses block index as page": ("int rc = kvfp4_oracle_dequantize_rows_f32(codes + pg * rows_per_page * (d / 2),",
+                                           "pg = b; int rc = kvfp4_oracle_dequantize_rows_f32(codes + pg * rows_per_page * (d / 2),"),
     "group amax from first row": ("for (int64_t i = 0; i < n; ++i) {\n    float v = fabsf", "for (int64_t i = 0; i < (n < 16 ? n : 16); ++i) {\n    float v = fabsf"),
     "attention scale ignored": ("s *= scale;", "s *= 1.0;"),
     "paged uses block index as page": ("int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),",
