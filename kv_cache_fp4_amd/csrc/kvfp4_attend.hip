@@ -59,20 +59,25 @@ __device__ __forceinline__ int vperm(int r) { return (r & 3) | ((r & 4) << 1) | 
 
 // Per-thread share of one 64-key step.  K: KU units (u = tid + kAtThreads r: key u / UPR,
 // d-chunk u % UPR).  V: VU pairs of consecutive keys of one d-chunk (p = tid + kAtThreads r:
-// d-chunk p / 32, keys 2 (p % 32) and 2 (p % 32) + 1).  Offsets are relative to the step's
-// first key and are the same for every step.
+// d-chunk p / 32, keys 2 (p % 32) and 2 (p % 32) + 1).  Offsets are byte offsets from the
+// step's first row and are the same for every step (32-bit, so the loads take a uniform
+// 64-bit base plus a per-lane 32-bit offset).  KEXACT / VEXACT: every thread has all its
+// units (no idle lanes), so full steps need no per-lane predicate.
 template <int D>
 struct Share {
   static constexpr int UPR = D / 8;
   static constexpr int KU = (kAtBN * UPR + kAtThreads - 1) / kAtThreads;
   static constexpr int VU = ((kAtBN / 2) * UPR + kAtThreads - 1) / kAtThreads;
+  static constexpr bool KEXACT = (kAtBN * UPR) % kAtThreads == 0;
+  static constexpr bool VEXACT = ((kAtBN / 2) * UPR) % kAtThreads == 0;
   int kkey[KU];            // key index in the step (>= kAtBN: no unit)
-  uint32_t koff[KU];       // code dword offset
-  uint32_t ksoff[KU];      // scale byte offset
+  int kj[KU];              // d-chunk
+  uint32_t kb[KU];         // code byte offset
+  uint32_t ksb[KU];        // scale byte offset
   int vkey[VU];            // first key of the pair (>= kAtBN: no pair)
   int vj[VU];              // d-chunk
-  uint32_t voff[VU][2];
-  uint32_t vsoff[VU][2];
+  uint32_t vb[VU][2];
+  uint32_t vsb[VU][2];
 };
 
 template <int D>
@@ -85,9 +90,10 @@ __device__ __forceinline__ void make_share(Share<D>& sh, int H, int head) {
     const int key = ui < kAtBN * Sh::UPR ? ui / Sh::UPR : kAtBN;
     const int j = ui % Sh::UPR;
     sh.kkey[r] = key;
+    sh.kj[r] = j;
     const uint32_t row = (uint32_t)((key < kAtBN ? key : 0) * H + head);
-    sh.koff[r] = row * Sh::UPR + j;
-    sh.ksoff[r] = row * (D / 16) + (j >> 1);
+    sh.kb[r] = (row * Sh::UPR + j) * 4u;
+    sh.ksb[r] = row * (D / 16) + (j >> 1);
   }
 #pragma unroll
   for (int r = 0; r < Sh::VU; ++r) {
@@ -99,8 +105,8 @@ __device__ __forceinline__ void make_share(Share<D>& sh, int H, int head) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint32_t row = (uint32_t)((2 * kp + kk) * H + head);
-      sh.voff[r][kk] = row * Sh::UPR + j;
-      sh.vsoff[r][kk] = row * (D / 16) + (j >> 1);
+      sh.vb[r][kk] = (row * Sh::UPR + j) * 4u;
+      sh.vsb[r][kk] = row * (D / 16) + (j >> 1);
     }
   }
 }
@@ -112,32 +118,44 @@ struct Raw {
   uint32_t vc[Share<D>::VU][2], vs[Share<D>::VU][2];
 };
 
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle; loads at byte offsets >= the resource's num_records return 0.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
+}
+
 // Load the packed data of the step whose first key is t0; `nk` = keys present in the step
-// (64 except in the last one).  Keys past the end read as code 0 / scale 0.
+// (64 except in the last one).  Each tensor is addressed through a buffer resource that
+// spans exactly the step's nk * H rows, so the per-lane 32-bit offsets need no address
+// arithmetic, and keys past the end fall outside the resource and read as code 0 / scale
+// 0 with no per-lane predicate.
 template <int D>
 __device__ __forceinline__ void load_raw(Raw<D>& r, const Share<D>& sh, int64_t t0, int nk, int H,
                                          const uint32_t* __restrict__ kcodes,
                                          const uint8_t* __restrict__ kscales,
                                          const uint32_t* __restrict__ vcodes,
                                          const uint8_t* __restrict__ vscales) {
+  using Sh = Share<D>;
   const int64_t row0 = t0 * H;
-  const uint32_t* kc = kcodes + row0 * (D / 8);
-  const uint8_t* ks = kscales + row0 * (D / 16);
-  const uint32_t* vc = vcodes + row0 * (D / 8);
-  const uint8_t* vs = vscales + row0 * (D / 16);
+  const uint32_t rows = (uint32_t)nk * (uint32_t)H;
+  const auto kc = raw_buffer((const uint8_t*)kcodes + row0 * (D / 2), rows * (D / 2));
+  const auto ks = raw_buffer(kscales + row0 * (D / 16), rows * (D / 16));
+  const auto vc = raw_buffer((const uint8_t*)vcodes + row0 * (D / 2), rows * (D / 2));
+  const auto vs = raw_buffer(vscales + row0 * (D / 16), rows * (D / 16));
 #pragma unroll
-  for (int i = 0; i < Share<D>::KU; ++i) {
-    const bool ok = sh.kkey[i] < nk;
-    r.kc[i] = ok ? kc[sh.koff[i]] : 0u;
-    r.ks[i] = ok ? (uint32_t)ks[sh.ksoff[i]] : 0u;
+  for (int i = 0; i < Sh::KU; ++i) {
+    r.kc[i] = __builtin_amdgcn_raw_buffer_load_b32(kc, (int)sh.kb[i], 0, 0);
+    r.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(ks, (int)sh.ksb[i], 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < Share<D>::VU; ++i)
+  for (int i = 0; i < Sh::VU; ++i)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bool ok = sh.vkey[i] + kk < nk;
-      r.vc[i][kk] = ok ? vc[sh.voff[i][kk]] : 0u;
-      r.vs[i][kk] = ok ? (uint32_t)vs[sh.vsoff[i][kk]] : 0u;
+      r.vc[i][kk] = __builtin_amdgcn_raw_buffer_load_b32(vc, (int)sh.vb[i][kk], 0, 0);
+      r.vs[i][kk] = __builtin_amdgcn_raw_buffer_load_b8(vs, (int)sh.vsb[i][kk], 0, 0);
     }
 }
 
@@ -162,17 +180,17 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
 #pragma unroll
   for (int i = 0; i < Share<D>::KU; ++i) {
     const int key = sh.kkey[i];
-    if (key < kAtBN) {
+    if (Share<D>::KEXACT || key < kAtBN) {
       float sd = key < sc.split ? sc.kd0 : sc.kd1;
       if constexpr (SHORT) sd = kamax[(t0 + key) / tpg] / kGlobalDiv;
-      const int j = (int)(sh.koff[i] % S::UPR);
-      *(uint4*)(k_buf + key * S::KSTR + j * 8) = decode8(raw.kc[i], e4m3_decode(raw.ks[i]) * sd);
+      *(uint4*)(k_buf + key * S::KSTR + sh.kj[i] * 8) =
+          decode8(raw.kc[i], e4m3_decode(raw.ks[i]) * sd);
     }
   }
 #pragma unroll
   for (int i = 0; i < Share<D>::VU; ++i) {
     const int key = sh.vkey[i];
-    if (key < kAtBN) {
+    if (Share<D>::VEXACT || key < kAtBN) {
       uint4 w[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -194,10 +212,23 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
   }
 }
 
-// Tracks the group of the current step's first key as the steps advance.
+// Tracks the group of the current step's first key as the steps advance, with the decode
+// scales of that group and the next (computed only when the group changes; a step of
+// kAtBN keys crosses at most one boundary when groups hold at least kAtBN tokens).
 struct GroupCursor {
-  int64_t g, bnd;  // group of the step's first key, first token of the next group
+  int64_t g, bnd;            // group of the step's first key, first token of the next group
+  float kd0, vd0, kd1, vd1;  // A/2688 of groups g and g+1 (g+1 clamped to the last group)
 };
+
+__device__ __forceinline__ void cursor_load(GroupCursor& gc, int64_t n_groups,
+                                            const float* __restrict__ kamax,
+                                            const float* __restrict__ vamax) {
+  const int64_t g1 = gc.g + 1 < n_groups ? gc.g + 1 : gc.g;
+  gc.kd0 = kamax[gc.g] / kGlobalDiv;
+  gc.vd0 = vamax[gc.g] / kGlobalDiv;
+  gc.kd1 = kamax[g1] / kGlobalDiv;
+  gc.vd1 = vamax[g1] / kGlobalDiv;
+}
 
 template <bool SHORT>
 __device__ __forceinline__ StepScales step_scales(GroupCursor& gc, int64_t t0, int64_t tpg,
@@ -208,16 +239,17 @@ __device__ __forceinline__ StepScales step_scales(GroupCursor& gc, int64_t t0, i
     sc.kd0 = sc.kd1 = sc.vd0 = sc.vd1 = 0.0f;
     sc.split = kAtBN;
   } else {
-    while (gc.bnd <= t0) {  // at most once per step when tpg >= kAtBN
+    if (gc.bnd <= t0) {  // steps advance by kAtBN <= tpg: at most one group per step
       ++gc.g;
       gc.bnd += tpg;
+      cursor_load(gc, n_groups, kamax, vamax);
     }
     const bool two = gc.bnd < t0 + kAtBN && gc.g + 1 < n_groups;
     sc.split = two ? (int)(gc.bnd - t0) : kAtBN;
-    sc.kd0 = kamax[gc.g] / kGlobalDiv;
-    sc.vd0 = vamax[gc.g] / kGlobalDiv;
-    sc.kd1 = two ? kamax[gc.g + 1] / kGlobalDiv : sc.kd0;
-    sc.vd1 = two ? vamax[gc.g + 1] / kGlobalDiv : sc.vd0;
+    sc.kd0 = gc.kd0;
+    sc.vd0 = gc.vd0;
+    sc.kd1 = gc.kd1;
+    sc.vd1 = gc.vd1;
   }
   return sc;
 }
@@ -264,14 +296,19 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
 
   Share<D> sh;
   make_share<D>(sh, H, head);
-  GroupCursor gc = {0, tpg};
+  GroupCursor gc;
+  gc.g = 0;
+  gc.bnd = tpg;
+  if constexpr (!SHORT) cursor_load(gc, n_groups, kamax, vamax);
   Raw<D> raw;
   const auto keys_in = [&](int64_t t) { return (int)(Tk - t < kAtBN ? Tk - t : kAtBN); };
-  load_raw<D>(raw, sh, 0, keys_in(0), H, kcodes, kscales, vcodes, vscales);
+  const auto load = [&](int64_t t) {
+    load_raw<D>(raw, sh, t, keys_in(t), H, kcodes, kscales, vcodes, vscales);
+  };
+  load(0);
   stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax), tpg,
                        kamax, vamax, k_lds[0], v_lds[0]);
-  if (kAtBN < Tk)
-    load_raw<D>(raw, sh, kAtBN, keys_in(kAtBN), H, kcodes, kscales, vcodes, vscales);
+  if (kAtBN < Tk) load(kAtBN);
   __syncthreads();
 
   int buf = 0;
@@ -294,8 +331,7 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
       const int64_t t1 = t0 + kAtBN;
       stage_tile<D, SHORT>(raw, sh, t1, step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax),
                            tpg, kamax, vamax, k_lds[buf ^ 1], v_lds[buf ^ 1]);
-      if (t1 + kAtBN < Tk)
-        load_raw<D>(raw, sh, t1 + kAtBN, keys_in(t1 + kAtBN), H, kcodes, kscales, vcodes, vscales);
+      if (t1 + kAtBN < Tk) load(t1 + kAtBN);
     }
 
     // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
