@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kAtWaves = 8;                  // waves per workgroup (2 per SIMD)
 constexpr int kAtThreads = 64 * kAtWaves;
@@ -172,7 +173,7 @@ struct StepScales {
 // blocks, two keys per 4-byte write (vperm keeps pairs together).
 template <int D, bool SHORT>
 __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh, int64_t t0,
-                                           const StepScales& sc, int64_t tpg,
+                                           const StepScales& sc, int64_t tpg, int64_t n_groups,
                                            const float* __restrict__ kamax,
                                            const float* __restrict__ vamax, __bf16* k_buf,
                                            __bf16* v_buf) {
@@ -182,7 +183,7 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
     const int key = sh.kkey[i];
     if (Share<D>::KEXACT || key < kAtBN) {
       float sd = key < sc.split ? sc.kd0 : sc.kd1;
-      if constexpr (SHORT) sd = kamax[(t0 + key) / tpg] / kGlobalDiv;
+      if constexpr (SHORT) sd = kamax[min((t0 + key) / tpg, n_groups - 1)] / kGlobalDiv;
       *(uint4*)(k_buf + key * S::KSTR + sh.kj[i] * 8) =
           decode8(raw.kc[i], e4m3_decode(raw.ks[i]) * sd);
     }
@@ -195,7 +196,7 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float sd = key + kk < sc.split ? sc.vd0 : sc.vd1;
-        if constexpr (SHORT) sd = vamax[(t0 + key + kk) / tpg] / kGlobalDiv;
+        if constexpr (SHORT) sd = vamax[min((t0 + key + kk) / tpg, n_groups - 1)] / kGlobalDiv;
         w[kk] = decode8(raw.vc[i][kk], e4m3_decode(raw.vs[i][kk]) * sd);
       }
       const int j = sh.vj[i];
@@ -239,7 +240,9 @@ __device__ __forceinline__ StepScales step_scales(GroupCursor& gc, int64_t t0, i
     sc.kd0 = sc.kd1 = sc.vd0 = sc.vd1 = 0.0f;
     sc.split = kAtBN;
   } else {
-    if (gc.bnd <= t0) {  // steps advance by kAtBN <= tpg: at most one group per step
+    // Steps advance by kAtBN <= tpg: at most one group per step.  (Steps past the end,
+    // which the loop stages harmlessly, stay on the last group.)
+    if (gc.bnd <= t0 && gc.g + 1 < n_groups) {
       ++gc.g;
       gc.bnd += tpg;
       cursor_load(gc, n_groups, kamax, vamax);
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   f32x16 o[S::DB];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) o[db] = f32x16{};
-  // Running max (base-2 logits) and running sum.  The max is only moved when a new score
-  // exceeds it by more than 8, so most steps skip the rescale of O; weights stay <= 2^8.
+  // Running max (base-2 logits) and running sum.  The max is only moved when a weight would
+  // exceed 2^8, so most steps skip the rescale of O.
   float m_run = -INFINITY, l_run = 0.0f;
 
   Share<D> sh;
@@ -301,21 +304,28 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   gc.bnd = tpg;
   if constexpr (!SHORT) cursor_load(gc, n_groups, kamax, vamax);
   Raw<D> raw;
-  const auto keys_in = [&](int64_t t) { return (int)(Tk - t < kAtBN ? Tk - t : kAtBN); };
+  // Keys of the step starting at t (0 past the end: its loads read nothing).
+  const auto keys_in = [&](int64_t t) {
+    return (int)(Tk - t >= kAtBN ? kAtBN : (Tk - t > 0 ? Tk - t : 0));
+  };
   const auto load = [&](int64_t t) {
     load_raw<D>(raw, sh, t, keys_in(t), H, kcodes, kscales, vcodes, vscales);
   };
   load(0);
   stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax), tpg,
-                       kamax, vamax, k_lds[0], v_lds[0]);
-  if (kAtBN < Tk) load(kAtBN);
+                       n_groups, kamax, vamax, k_lds[0], v_lds[0]);
+  load(kAtBN);
   __syncthreads();
 
   int buf = 0;
   for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN, buf ^= 1) {
     const __bf16* kb = k_lds[buf];
     const __bf16* vb = v_lds[buf];
-    // S^T = K Q^T for 64 keys (two 32-key row blocks) x the wave's 32 queries.
+    const int64_t t1 = t0 + kAtBN;
+    const StepScales sc = step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax);
+    // One basic block: S^T = K Q^T for 64 keys (two 32-key row blocks) x the wave's 32
+    // queries; the next step dequantized into the other buffer (unconditionally: past the
+    // end it stages zeros that nobody reads); the loads of the step after.
     f32x16 s[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -326,18 +336,12 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kc], s[rb], 0, 0, 0);
       }
     }
-    // Next step: dequantize into the other buffer, then start the loads of the one after.
-    if (t0 + kAtBN < Tk) {
-      const int64_t t1 = t0 + kAtBN;
-      stage_tile<D, SHORT>(raw, sh, t1, step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax),
-                           tpg, kamax, vamax, k_lds[buf ^ 1], v_lds[buf ^ 1]);
-      if (t1 + kAtBN < Tk) load(t1 + kAtBN);
-    }
+    stage_tile<D, SHORT>(raw, sh, t1, sc, tpg, n_groups, kamax, vamax, k_lds[buf ^ 1],
+                         v_lds[buf ^ 1]);
+    load(t1 + kAtBN);
 
     // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
-    // > 0, so the max is taken on the raw scores and scaled once.  Keys past Tk (last step
-    // only) are masked to -inf.
-    float mx = -INFINITY;
+    // > 0 and m the running max of c s.  Keys past Tk (last step only) are masked to -inf.
     if (t0 + kAtBN > Tk) {
       const int nk = (int)(Tk - t0);
 #pragma unroll
@@ -348,29 +352,51 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
           if (key >= nk) s[rb][j] = -INFINITY;
         }
     }
+    // Weights against the current running max, packed to bf16 (the B operand of O^T += V^T
+    // P^T), and this lane's share of their sum, accumulated from the same bf16 values with
+    // dot2 against (1, 1).
+    bf16x8 pb[2][2];
+    const auto weights = [&]() {
+      float sum = 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[rb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * qk_scale_log2;
-    // Move the running max (and rescale O and l) only when some query of the wave needs it.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[rb][8 * s2 + i], qk_scale_log2, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[rb][8 * s2 + i + 1], qk_scale_log2, -m_run));
+            const f32x2 pp = {p0, p1};
+            const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+            pb[rb][s2][i] = pk.x;
+            pb[rb][s2][i + 1] = pk.y;
+            sum = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes2, sum, false);
+          }
+      return sum;
+    };
+    float ps = weights();
+    // The running max moves (and O and l are rescaled) only when some weight of the wave
+    // exceeds 2^8 -- detected from the lane sums, which exceed 2^8 if any term does (and are
+    // +inf or NaN on the first step, where the running max is still -inf).  Then the weights
+    // are recomputed against the new max.  If a sum exceeds 2^8 the step's max is above the
+    // running max, so the max always moves forward.
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 256.0f)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[rb][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * qk_scale_log2;
       const float m_new = fmaxf(m_run, mx);  // finite: key t0 < Tk is in this step
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) o[db] *= alpha;
+      ps = weights();
     }
-    float ps = 0.0f;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][j], qk_scale_log2, -m_run));
-        s[rb][j] = p;
-        ps += p;
-      }
     l_run += ps;
 
     // O^T += V^T P^T, 16 keys per MFMA.
@@ -378,14 +404,11 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[rb][8 * s2 + i];
 #pragma unroll
         for (int db = 0; db < S::DB; ++db) {
           const bf16x8 a = *(const bf16x8*)(vb + (32 * db + l32) * S::VSTR + 32 * rb +
                                             16 * s2 + 8 * hh);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][s2], o[db], 0, 0, 0);
         }
       }
     __syncthreads();  // the other buffer is complete; this one may be overwritten next step
