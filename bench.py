@@ -37,7 +37,7 @@ def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C3", choices=["C1", "C2", "C3", "C4"])
     ap.add_argument("--rule", default=None, choices=["static_6", "static_4", "mse"],
                     help="append rule (default: mse for C3, static_6 otherwise)")
@@ -304,9 +304,10 @@ def bench_f32_fake(w, device, steps=20, warmup=3):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_attend(device, steps=20, warmup=3):
+def bench_attend(device, steps=50, warmup=50):
     """Q [4680, 12, 128] against the 32760-token NVFP4 K/V cache (7 groups of 4680 tokens,
-    static_6), non-causal, softmax scale 1/sqrt(128): 4*Tq*Tk*H*D flops per call."""
+    static_6), non-causal, softmax scale 1/sqrt(128): 4*Tq*Tk*H*D flops per call.  The MFMA
+    clock takes some 40 calls (~40 ms) to settle from idle, hence the long warmup."""
     import torch
 
     import kv_cache_fp4_amd as kv
