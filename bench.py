@@ -299,6 +299,38 @@ def bench_f32_fake(w, device, steps=20, warmup=3):
     return res
 
 
+def cpu_baseline_attend(budget_s=6.0):
+    """The attention oracle (double precision softmax(QK^T)V over the oracle's own bf16
+    dequantization of the static_6 cache) on a sample of query rows of the attention
+    workload, single-threaded; quantize/dequantize of K and V happen before the clock."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    cfg = synth.C5
+    H, D, Tk = cfg.heads, cfg.head_dim, cfg.cache_tokens
+    kvh = []
+    for kv_ in (0, 1):
+        x = torch.cat([synth.chunk_group(cfg, 0, kv_, c) for c in range(cfg.chunks)])
+        xh = x.reshape(-1, D).view(torch.int16).numpy().view(np.uint16)
+        c, s_, a = oracle.quantize(xh, cfg.rows_per_group, "static_6")
+        kvh.append(oracle.dequantize(c, s_, a, cfg.rows_per_group).reshape(Tk, H, D))
+    q = synth.c5_query().view(torch.int16).numpy().view(np.uint16)
+    rng = np.random.default_rng(5)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = rng.integers(0, synth.C5_Q_TOKENS * H, 8)
+        oracle.attend_rows(q, kvh[0], kvh[1], D ** -0.5, rows)
+        done += rows.size
+    dt = time.perf_counter() - t0
+    flops = 4.0 * done * Tk * D
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} query rows (of {synth.C5_Q_TOKENS * H}) of {cfg.name}, each against all "
+                       f"{Tk} keys, in {dt:.1f} s, single-threaded C oracle (double)")}
+
+
 # ---- fused dequantize + attention (its own workload) ---------------------------------------
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -422,6 +454,19 @@ def main(argv=None):
     ms_dq = sum(a.elapsed_time(b) for a, b in dq) / args.steps
     ms_ap = sum(a.elapsed_time(b) for a, b in ap) / args.steps
 
+    # The same cache read as 60 launches of one layer-tensor each (7 groups, contiguous), as a
+    # model that attends layer by layer would issue them.
+    gpl = cfg.chunks  # groups per layer-tensor
+    n_launch = w.n_groups // gpl
+    rpl = gpl * w.rpg
+
+    def per_layer():
+        for i in range(n_launch):
+            r0, r1 = i * rpl, (i + 1) * rpl
+            w.kv.kvfp4_dequantize(w.codes[r0:r1], w.scales[r0:r1], w.amax[i * gpl:(i + 1) * gpl],
+                                  w.rpg, y=w.out[r0:r1])
+    ms_pl = _time_calls(per_layer, dev, max(args.steps // 3, 3), 2)
+
     step_bytes = w.append_bytes() + w.dequant_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     dq_gbs = w.dequant_bytes() / (ms_dq * 1e-3) / 1e9
@@ -457,6 +502,9 @@ def main(argv=None):
         "breakdown": {"append_ms": round(ms_ap, 4), "append_GBps": round(ap_gbs, 2),
                       "append_bytes": w.append_bytes(),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
+        "per_layer_dequant": {"launches": n_launch, "ms_total": round(ms_pl, 4),
+                              "us_per_launch": round(1e3 * ms_pl / n_launch, 2),
+                              "GBps": round(w.dequant_bytes() / (ms_pl * 1e-3) / 1e9, 2)},
     }
     if not args.no_f32_fake:
         print("bench: timing float32 dequantize and fake quantize", file=sys.stderr, flush=True)
@@ -474,6 +522,8 @@ def main(argv=None):
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, rule)
         res["cpu_baseline"]["host_threads_available"] = os.cpu_count()
+        if not args.no_attend:
+            res["attend"]["cpu_baseline"] = cpu_baseline_attend()
     print(json.dumps(res), flush=True)
 
 
