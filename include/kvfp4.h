@@ -34,7 +34,7 @@
  *     enqueued, the call returns before it runs;
  *   - argument errors are detected on the host and returned before anything is enqueued;
  *     rows == 0 (or q_tokens == 0) is a no-op that returns KVFP4_OK;
- *   - inputs and outputs must not overlap;
+ *   - inputs and outputs must not overlap (kvfp4_fake_quantize alone allows y == x);
  *   - no C++ exception crosses the ABI.
  */
 #ifndef KVFP4_H
@@ -115,8 +115,8 @@ int kvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g
  *   O[t, h, :] = sum_j softmax_j(softmax_scale * <Q[t, h, :], K[j, h, :]>) V[j, h, :]
  * per head h, non-causal, where K and V are the dequantized packed caches (exactly the
  * bf16 values kvfp4_dequantize would produce).  Scores, softmax and accumulation are fp32
- * (bf16 MFMA inputs; the softmax weights are rounded to bf16 for the second product); the
- * output is rounded to bf16.
+ * (bf16 MFMA inputs; the softmax weights are rounded to bf16 for the second product, and
+ * the row sums are taken over those same bf16 weights); the output is rounded to bf16.
  *
  *   q                 bf16 [q_tokens, heads, head_dim]; 16-byte aligned
  *   k_codes, v_codes  uint8 [kv_tokens, heads, head_dim/2]; 16-byte aligned
