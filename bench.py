@@ -494,6 +494,8 @@ def main(argv=None):
                    "elements_per_step": w.append_elems + w.cache_elems,
                    "bytes_per_step": step_bytes, "generator_version": synth.GENERATOR_VERSION},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        # the same step counted without the scale bytes (bf16 + codes only, 2.5 B/element)
+        "GBps_without_scale_bytes": round((w.append_elems + w.cache_elems) * 2.5 / (ms_step * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "dequant_kernel",
                      "achieved": round(dq_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dq_gbs / HBM_PEAK_GBS, 4),
