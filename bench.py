@@ -404,10 +404,9 @@ def traffic_for(workload_name):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
-              "dequantize path has no communication and the quantize path would need one "
-              "max-allreduce of the group amax per append -- see the sharding notes in DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); sharded by heads, the "
+              "dequantize and attention paths need no communication and the quantize path one "
+              "max-allreduce of the group amax per append, which is not built", file=sys.stderr)
         sys.exit(2)
     import torch
 
