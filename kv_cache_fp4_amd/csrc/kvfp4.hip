@@ -664,6 +664,8 @@ static int check_paged(int64_t n_blocks, int64_t rows_per_page, int32_t head_dim
   int64_t ng = 0;
   int rc = check_shape(n_blocks * rows_per_page, head_dim, rows_per_page, &ng);
   if (rc != KVFP4_OK) return rc;
+  // the packed side (n_pages pages) obeys the same size limit as the dense side
+  if (n_pages > 0 && rows_per_page > ((INT64_C(1) << 52) / head_dim) / n_pages) return KVFP4_EINVAL;
   if (n_blocks > 0 && !block_table) return KVFP4_EINVAL;
   if (n_blocks > 0 && !aligned(block_table, 4)) return KVFP4_EALIGN;
   return KVFP4_OK;

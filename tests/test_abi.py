@@ -148,6 +148,7 @@ def dqp(codes=A16, scales=A16, amax=A16, tab=A16, nb=4, rpp=24, d=128, npg=8, y=
     (dict(d=100), KVFP4_EUNSUPPORTED), (dict(tab=A16 + 2), KVFP4_EALIGN),
     (dict(codes=A16 + 8), KVFP4_EALIGN), (dict(amax=A16 + 1), KVFP4_EALIGN),
     (dict(nb=1 << 40, rpp=1 << 20), KVFP4_EINVAL),
+    (dict(npg=1 << 40, rpp=1 << 10), KVFP4_EINVAL),
 ])
 def test_quantize_paged_rejects(kw, want):
     assert qp(**kw) == want
@@ -156,7 +157,7 @@ def test_quantize_paged_rejects(kw, want):
 @pytest.mark.parametrize("kw,want", [
     (dict(nb=-1), KVFP4_EINVAL), (dict(rpp=-2), KVFP4_EINVAL), (dict(tab=None), KVFP4_EINVAL),
     (dict(y=None), KVFP4_EINVAL), (dict(d=32), KVFP4_EUNSUPPORTED), (dict(y=A16 + 4), KVFP4_EALIGN),
-    (dict(scales=A16 + 3), KVFP4_EALIGN),
+    (dict(scales=A16 + 3), KVFP4_EALIGN), (dict(npg=1 << 40, rpp=1 << 10), KVFP4_EINVAL),
 ])
 def test_dequantize_paged_rejects(kw, want):
     assert dqp(**kw) == want
