@@ -1,0 +1,21 @@
+"""The library used from plain C: tests/c_abi/abi_roundtrip.c (built by __graft_entry__.build())
+allocates device buffers with hipMalloc, runs quantize + dequantize on a stream of its own
+for every rule and three group layouts, compares every output byte with the oracle, and
+checks host-side argument errors.  It runs as its own process (its own HIP runtime)."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "abi_roundtrip")
+
+
+def test_c_program_round_trip_matches_oracle():
+    if not os.path.exists(EXE):
+        pytest.fail("tests/c_abi/abi_roundtrip not built (run __graft_entry__.build())")
+    r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().endswith("OK")
+    assert r.stdout.count("bit-exact") == 9
