@@ -97,6 +97,13 @@ __device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
   __builtin_nontemporal_store(t, (u32x4*)p);
 }
 
+// Streaming 16-byte load with the non-temporal hint (measured: faster for the group amax
+// pass, slower for the encode passes, which read the same data right after).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // ---- kernel 1: clear group amax (through the block table when there is one) --------------
 __global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int64_t n,
                                                     const int32_t* __restrict__ table,
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restr
 #pragma unroll
     for (int k = 0; k < kAmaxUnroll; ++k) {
       const int64_t u = base + k * 64 + lane;
-      v[k] = (u < r.end) ? x[u] : make_uint4(0, 0, 0, 0);
+      v[k] = (u < r.end) ? load_nt(x + u) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < kAmaxUnroll; ++k) mx = max(mx, absmax8_bits(v[k]));
