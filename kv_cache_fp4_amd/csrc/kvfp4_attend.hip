@@ -176,7 +176,7 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
                                            const StepScales& sc, int64_t tpg, int64_t n_groups,
                                            const float* __restrict__ kamax,
                                            const float* __restrict__ vamax, __bf16* k_buf,
-                                           __bf16* v_buf) {
+                                           __bf16* v_buf, const float* e4m3_tab) {
   using S = AttShape<D>;
 #pragma unroll
   for (int i = 0; i < Share<D>::KU; ++i) {
@@ -185,7 +185,7 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
       float sd = key < sc.split ? sc.kd0 : sc.kd1;
       if constexpr (SHORT) sd = kamax[min((t0 + key) / tpg, n_groups - 1)] / kGlobalDiv;
       *(uint4*)(k_buf + key * S::KSTR + sh.kj[i] * 8) =
-          decode8(raw.kc[i], e4m3_decode(raw.ks[i]) * sd);
+          decode8(raw.kc[i], e4m3_tab[raw.ks[i]] * sd);
     }
   }
 #pragma unroll
@@ -197,7 +197,7 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
       for (int kk = 0; kk < 2; ++kk) {
         float sd = key + kk < sc.split ? sc.vd0 : sc.vd1;
         if constexpr (SHORT) sd = vamax[min((t0 + key + kk) / tpg, n_groups - 1)] / kGlobalDiv;
-        w[kk] = decode8(raw.vc[i][kk], e4m3_decode(raw.vs[i][kk]) * sd);
+        w[kk] = decode8(raw.vc[i][kk], e4m3_tab[raw.vs[i][kk]] * sd);
       }
       const int j = sh.vj[i];
       const int pos = (key & ~15) | vperm(key & 15);
@@ -297,6 +297,10 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   // exceed 2^8, so most steps skip the rescale of O.
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // The 127 E4M3 scale values (exact), looked up instead of decoded per unit.
+  __shared__ float e4m3_tab[128];
+  if (tid < 128) e4m3_tab[tid] = e4m3_decode((uint32_t)tid);
+  __syncthreads();
   Share<D> sh;
   make_share<D>(sh, H, head);
   GroupCursor gc;
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   };
   load(0);
   stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax), tpg,
-                       n_groups, kamax, vamax, k_lds[0], v_lds[0]);
+                       n_groups, kamax, vamax, k_lds[0], v_lds[0], e4m3_tab);
   load(kAtBN);
   __syncthreads();
 
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
       }
     }
     stage_tile<D, SHORT>(raw, sh, t1, sc, tpg, n_groups, kamax, vamax, k_lds[buf ^ 1],
-                         v_lds[buf ^ 1]);
+                         v_lds[buf ^ 1], e4m3_tab);
     load(t1 + kAtBN);
 
     // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
