@@ -9,8 +9,12 @@ to bf16.  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is algorithmic bytes per step / time per step, where the
 bytes per element are bf16 (2) + codes (0.5) + scales (0.0625), plus 4 B per group amax.
+Beside the step it reports (each on its own workload, skippable with --no-*): the same
+cache read as per-layer launches, float32 dequantize and fake quantization, the RTN
+INT4/INT2 caches, the paged-cache gather, the fused dequantize + attention, and the CPU
+oracle on bounded samples.
 
-    python bench.py [--steps K] [--warmup W] [--config C3|C4|C2|C1] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config C3|C4|C2|C1] [--rule R] [--gpus 1]
 """
 from __future__ import annotations
 
