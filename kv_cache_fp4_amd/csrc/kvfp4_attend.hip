@@ -13,7 +13,7 @@
 //
 // Computation: O = softmax(scale * Q K^T) V per head, non-causal, fp32 accumulation and
 // an online (running max / running sum) softmax in fp32; P is rounded to bf16 for the
-// second product; O is rounded to bf16.
+// second product and the row sums are taken over those bf16 weights; O is rounded to bf16.
 //
 // Mapping (v_mfma_f32_32x32x16_bf16; a lane holds 8 consecutive k of one row of A and of
 // one column of B; accumulator register j of lane l is row 8*(j/4) + 4*(l/32) + j%4,
@@ -21,7 +21,8 @@
 //   - a workgroup is 8 waves x 32 queries of one head; a step covers 64 keys;
 //   - S^T = K Q^T: A = K rows from LDS, B = the wave's Q^T held in registers, so each lane
 //     ends up owning one query (column) and 32 of the 64 keys of the step; the other 32
-//     keys of that query sit in lane l ^ 32, one exchange gives the row max / row sum;
+//     keys of that query sit in lane l ^ 32, and one exchange combines the two halves
+//     (of the final row sum, and of the row max on the rare steps that move it);
 //   - O^T = V^T P^T: B = P^T comes straight from the S^T registers (rounded to bf16), A =
 //     V^T read from LDS, where V is stored transposed with bits 2 and 3 of the key index
 //     swapped inside each 16-key block so that the 8 keys a lane needs are contiguous;
