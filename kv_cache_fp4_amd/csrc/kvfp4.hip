@@ -41,6 +41,7 @@ constexpr int kAmaxThreads = 512, kAmaxUnroll = 4, kAmaxSteps = 4;
 constexpr int kQuantThreads = 128, kQuantUnroll = 2, kQuantSteps = 1;  // static rules
 constexpr int kMseThreads = 256, kMseUnroll = 2, kMseSteps = 4;        // mse rule
 constexpr int kDqThreads = 128, kDqUnroll = 2;                         // one step
+constexpr int kDqPagedThreads = 512;  // paged gather: one page lookup per 1024 units
 
 constexpr int64_t tile_units(int threads, int unroll, int steps) {
   return (int64_t)threads * unroll * steps;
@@ -287,11 +288,15 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* x,
 
 // ---- dequantize ([P-NVFP4] "Stage 3"; [P-KV] "CUDA De-quantization Pipeline") -----------
 
-// One step per workgroup: two waves, each writing one contiguous 2 KiB run of bf16.
-__global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
-                                                             const uint8_t* __restrict__ scales,
-                                                             const float* __restrict__ amax,
-                                                             uint4* __restrict__ y, Part p) {
+// One step per workgroup: THREADS/64 waves, each writing one contiguous 2 KiB run of bf16.
+// Dense reads use two-wave workgroups; the paged gather uses eight-wave ones, because each
+// of its workgroups must look its page up before its loads can issue (measured: 5.85 ->
+// 6.0 TB/s on random 16-token pages).
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void dequant_kernel(const uint32_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ amax,
+                                                          uint4* __restrict__ y, Part p) {
   const Range r = wg_range(p);
   if (r.beg >= r.end) return;  // uniform: skipped page or empty slice
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -575,17 +580,21 @@ int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
 int dequantize_impl(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
                     int64_t rows, int32_t head_dim, int64_t rpg, const int32_t* table,
                     int64_t n_pages, uint16_t* y16, float* y32, hipStream_t s) {
+  const int threads = (table && !y32) ? kDqPagedThreads : kDqThreads;
   Part part;
   unsigned grid = 0;
-  int rc = plan(rows, head_dim, rpg, tile_units(kDqThreads, kDqUnroll, 1), &part, &grid);
+  int rc = plan(rows, head_dim, rpg, tile_units(threads, kDqUnroll, 1), &part, &grid);
   if (rc != KVFP4_OK) return rc;
   part.table = table;
   if (table) part.n_pages = n_pages;
   if (y32)
     hipLaunchKernelGGL(dequant_f32_kernel, dim3(grid), dim3(kDqfThreads), 0, s,
                        (const uint16_t*)codes, scales, group_amax, (float4*)y32, part);
+  else if (table)
+    hipLaunchKernelGGL(dequant_kernel<kDqPagedThreads>, dim3(grid), dim3(kDqPagedThreads), 0, s,
+                       (const uint32_t*)codes, scales, group_amax, (uint4*)y16, part);
   else
-    hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDqThreads), 0, s,
+    hipLaunchKernelGGL(dequant_kernel<kDqThreads>, dim3(grid), dim3(kDqThreads), 0, s,
                        (const uint32_t*)codes, scales, group_amax, (uint4*)y16, part);
   return launched();
 }
