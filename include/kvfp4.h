@@ -29,7 +29,8 @@
  * Conventions for every entry point:
  *   - pointers are DEVICE pointers unless stated; the caller allocates and frees all of
  *     them; the library never allocates, never synchronizes, keeps no state besides a
- *     thread-local copy of the last HIP error, and is reentrant across streams;
+ *     thread-local copy of the last HIP error and the two process-wide options of
+ *     kvfp4_set_option, and is reentrant across streams;
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work is only
  *     enqueued, the call returns before it runs;
  *   - argument errors are detected on the host and returned before anything is enqueued;
@@ -84,7 +85,11 @@ enum kvfp4_rule {
  *   scales  (out)   uint8 [rows, head_dim/16]; 4-byte aligned
  *   group_amax (out) float [ceil(rows/rows_per_group)]; 4-byte aligned
  * Appending a chunk to a cache = passing pointers offset to the chunk's first row and
- * group.  Inputs must be finite.  Enqueues three kernels (amax clear, group amax, encode).
+ * group.  Inputs must be finite.  Enqueues three kernels: when every group (the last one
+ * included) has at least 528 elements, a hand-off clear, one kernel that computes the group
+ * amax and encodes (it borrows three dwords of each group's codes for the hand-off; the
+ * codes are complete when the call's work ends), and a finish kernel; otherwise amax
+ * clear, group amax, encode.  Both give the same bytes.
  */
 int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
                    int32_t rule, uint8_t* codes, uint8_t* scales, float* group_amax,
@@ -228,6 +233,26 @@ int kvfp4_rtn_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t r
  * above.  Any output pointer may be NULL. */
 int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
                        int64_t* codes_bytes, int64_t* scales_bytes, int64_t* n_groups);
+
+/*
+ * Process-wide options, read when a call enqueues its work (work already enqueued or
+ * captured in a graph keeps the values it was enqueued with).  Neither changes any output.
+ *   KVFP4_OPT_APPEND_FUSED    1 (default): kvfp4_quantize and kvfp4_fake_quantize (not in
+ *                             place) take the one-kernel amax + encode form where it
+ *                             applies; 0: always the three-kernel form.
+ *   KVFP4_OPT_APPEND_WAIT_US  in the one-kernel form, the longest time (microseconds) an
+ *                             encode workgroup waits for its group amax before computing it
+ *                             itself from the input; 0 = never wait; default 20000, at
+ *                             most 60000000.
+ * kvfp4_set_option returns KVFP4_EINVAL for an unknown option or a value out of range;
+ * kvfp4_get_option writes the current value to *value (host pointer).
+ */
+enum kvfp4_option {
+  KVFP4_OPT_APPEND_FUSED = 1,
+  KVFP4_OPT_APPEND_WAIT_US = 2
+};
+int kvfp4_set_option(int32_t option, int64_t value);
+int kvfp4_get_option(int32_t option, int64_t* value);
 
 /* Diagnostics. */
 const char* kvfp4_status_str(int status); /* static string, never NULL */

@@ -60,6 +60,10 @@ def _load() -> ctypes.CDLL:
     L.kvfp4_abi_version.restype = ctypes.c_int
     L.kvfp4_last_hip_error.argtypes = []
     L.kvfp4_last_hip_error.restype = ctypes.c_int
+    L.kvfp4_set_option.argtypes = [i32, i64]
+    L.kvfp4_set_option.restype = ctypes.c_int
+    L.kvfp4_get_option.argtypes = [i32, ctypes.POINTER(i64)]
+    L.kvfp4_get_option.restype = ctypes.c_int
     return L
 
 
@@ -105,6 +109,21 @@ def kvfp4_packed_sizes(rows: int, head_dim: int, rows_per_group: int):
     _check(lib.kvfp4_packed_sizes(rows, head_dim, rows_per_group, ctypes.byref(c),
                                   ctypes.byref(s), ctypes.byref(g)))
     return c.value, s.value, g.value
+
+
+OPTIONS = {"append_fused": 1, "append_wait_us": 2}
+
+
+def kvfp4_set_option(name, value: int) -> None:
+    """Set a process-wide option ("append_fused" 0/1, "append_wait_us" >= 0)."""
+    _check(lib.kvfp4_set_option(OPTIONS[name] if isinstance(name, str) else int(name), int(value)))
+
+
+def kvfp4_get_option(name) -> int:
+    v = ctypes.c_int64()
+    _check(lib.kvfp4_get_option(OPTIONS[name] if isinstance(name, str) else int(name),
+                                ctypes.byref(v)))
+    return v.value
 
 
 def kvfp4_quantize(x, rows_per_group: int, rule="static_6", codes=None, scales=None,
@@ -271,4 +290,5 @@ def kvfp4_attend(q, k_codes, k_scales, k_amax, v_codes, v_scales, v_amax,
 __all__ = ["kvfp4_quantize", "kvfp4_dequantize", "kvfp4_dequantize_f32", "kvfp4_fake_quantize",
            "kvfp4_quantize_paged", "kvfp4_dequantize_paged", "kvfp4_dequantize_paged_f32",
            "kvfp4_rtn_quantize", "kvfp4_rtn_dequantize", "kvfp4_attend", "kvfp4_packed_sizes",
-           "KVFP4Error", "RULES", "lib", "LIB_PATH"]
+           "kvfp4_set_option", "kvfp4_get_option", "KVFP4Error", "RULES", "OPTIONS", "lib",
+           "LIB_PATH"]

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvfp4.h"
 #include "kvfp4_device.hpp"
 
@@ -224,6 +226,31 @@ __device__ __forceinline__ float half_err(const float xf[8], const Cand& c) {
   return e;
 }
 
+// Encode one unit (8 elements, this lane) of a 16-element block whose other half is in the
+// partner lane (lane ^ 1); both lanes must make the call.  Returns the chosen candidate.
+template <int RULE>
+__device__ __forceinline__ Cand encode_unit(uint4 v, float s_enc, const Tables* tb) {
+  const float xf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  // Block amax: this lane's 8 elements, then the partner lane's.
+  uint32_t mb = absmax8_bits(v);
+  mb = max(mb, swap_pair(mb));
+  if constexpr (RULE == KVFP4_RULE_STATIC6) {
+    return make_cand<6>(xf, mb, s_enc, tb);
+  } else if constexpr (RULE == KVFP4_RULE_STATIC4) {
+    return make_cand<4>(xf, mb, s_enc, tb);
+  } else {
+    const Cand c6 = make_cand<6>(xf, mb, s_enc, tb);
+    const Cand c4 = make_cand<4>(xf, mb, s_enc, tb);
+    // err = (chain over elements 0..7) + (chain over 8..15); a sum of two values is the
+    // same in either operand order, so both lanes of the pair agree.
+    const float h6 = half_err(xf, c6), h4 = half_err(xf, c4);
+    const float err6 = h6 + swap_pair(h6);
+    const float err4 = h4 + swap_pair(h4);
+    return (err4 < err6) ? c4 : c6;
+  }
+}
+
 // FAKE: instead of storing codes and scale bytes, store the block dequantized to bf16
 // (decode8 with the chosen candidate's S, which is E4M3(sf) * s_dec exactly as the
 // dequantize kernel computes it), so the output equals dequantize(quantize(x)).
@@ -252,27 +279,7 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* x,
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int64_t u = base + k * 64 + lane;
-      const float xf[8] = {bf16_lo(v[k].x), bf16_hi(v[k].x), bf16_lo(v[k].y), bf16_hi(v[k].y),
-                           bf16_lo(v[k].z), bf16_hi(v[k].z), bf16_lo(v[k].w), bf16_hi(v[k].w)};
-      // Block amax: this lane's 8 elements, then the partner lane's (the two lanes of a
-      // pair hold the two halves of one 16-element block; all lanes execute the swap).
-      uint32_t mb = absmax8_bits(v[k]);
-      mb = max(mb, swap_pair(mb));
-      Cand pick;
-      if constexpr (RULE == KVFP4_RULE_STATIC6) {
-        pick = make_cand<6>(xf, mb, s_enc, &tabs);
-      } else if constexpr (RULE == KVFP4_RULE_STATIC4) {
-        pick = make_cand<4>(xf, mb, s_enc, &tabs);
-      } else {
-        const Cand c6 = make_cand<6>(xf, mb, s_enc, &tabs);
-        const Cand c4 = make_cand<4>(xf, mb, s_enc, &tabs);
-        // err = (chain over elements 0..7) + (chain over 8..15); a sum of two values is
-        // the same in either operand order, so both lanes of the pair agree.
-        const float h6 = half_err(xf, c6), h4 = half_err(xf, c4);
-        const float err6 = h6 + swap_pair(h6);
-        const float err4 = h4 + swap_pair(h4);
-        pick = (err4 < err6) ? c4 : c6;
-      }
+      const Cand pick = encode_unit<RULE>(v[k], s_enc, &tabs);
       if (u < r.end) {
         if constexpr (FAKE) {
           store_nt(fake_y + u, decode8(pick.codes, pick.S));
@@ -283,6 +290,222 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(const uint4* x,
         }
       }
     }
+  }
+}
+
+// ---- one-launch append: group amax and encode in a single kernel ------------------------
+//
+// The three-kernel form above reads the input twice from HBM (amax pass, then encode).  Here
+// one launch does both.  Work items in workgroup index (= dispatch) order: the amax tiles of
+// group g + L come before the encode tiles of group g, L = ceil(32 MiB / group input bytes)
+// groups (at least 1, at most all), so an encode tile re-reads input that was read shortly
+// before and is still in the 256 MB Infinity Cache.
+//
+// Per group, three dwords inside the group's own output (the code dwords of its units 0, 32
+// and 64, or the first dword of those units of the bf16 output for fake quantization: three
+// different 128-byte lines), zeroed by append_clear_kernel before the launch, carry the
+// hand-off from the amax tiles to the encode tiles:
+//   count  (unit 0)   amax tiles done
+//   max    (unit 32)  max over the done tiles of their 15-bit magnitude patterns << 16
+//   ready  (unit 64)  final amax bits | 1, stored by the tile that completes the count
+// An amax tile folds its max into `max`, then adds 1 to `count`; the add takes the returned
+// old max as an operand, so it is issued only after the max has been performed.  The tile
+// whose add completes the count reads `max` (now final), stores the group amax and sets
+// `ready`.  All of these are device-scope atomics, coherent across the XCDs.
+// An encode tile polls `ready` for at most `wait_ticks` wall-clock ticks (a short sleep
+// between polls); past that it computes the group max from x itself -- the same value -- so
+// the bound limits the wait and never changes a result.  Encode tiles skip the stores of
+// units 0, 32 and 64 of their group; append_finish_kernel encodes those three units after the
+// launch, overwriting the words.  Requires every group (the last included) to have at least
+// 66 units.
+constexpr int kAppendATile = 4096;  // units per amax tile
+constexpr int kAppendETile = 2048;  // units per encode tile
+constexpr int64_t kAppendLagUnits = (INT64_C(32) << 20) / 16;
+constexpr int kAppendStaticThreads = 512, kAppendMseThreads = 256;  // measured
+
+struct Append {
+  int64_t units_total, units_per_group;
+  uint32_t n_groups, lag;        // lag: groups, in [1, n_groups]
+  uint32_t a_tiles, e_tiles;     // per group
+  uint64_t wait_ticks;
+};
+
+// Max of the 15-bit magnitude patterns over units [beg, end), per thread.
+template <int THREADS>
+__device__ __forceinline__ uint32_t thread_absmax(const uint4* x, int64_t beg, int64_t end) {
+  constexpr int kU = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t mx = 0;
+  for (int64_t base = beg + wave * 64 * kU; base < end; base += THREADS * kU) {
+    uint4 v[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      v[k] = (u < end) ? x[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) mx = max(mx, absmax8_bits(v[k]));
+  }
+  return mx;
+}
+
+// Workgroup max; every thread gets it.  `red` must not be in use by another reduction.
+template <int THREADS>
+__device__ __forceinline__ uint32_t workgroup_max(uint32_t mx, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < THREADS / 64; ++w) m = max(m, red[w]);
+  return m;
+}
+
+// Dword of the hand-off word at unit `unit` of the output (codes: one dword per unit; fake
+// bf16 output: four dwords per unit).
+template <bool FAKE>
+__device__ __forceinline__ uint32_t* handoff_word(uint32_t* out, int64_t unit) {
+  return out + unit * (FAKE ? 4 : 1);
+}
+
+__global__ __launch_bounds__(256) void append_clear_kernel(uint32_t* __restrict__ out,
+                                                           int64_t units_per_group,
+                                                           int64_t n_groups, int stride) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 3 * n_groups;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t g = i / 3, k = i - g * 3;
+    out[(g * units_per_group + 32 * k) * stride] = 0u;
+  }
+}
+
+template <int RULE, int THREADS, bool FAKE>
+__global__ __launch_bounds__(THREADS) void append_kernel(const uint4* __restrict__ x,
+                                                         uint32_t* __restrict__ amax_bits,
+                                                         uint32_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales,
+                                                         uint4* __restrict__ fake_y, Append f) {
+  // work item of this workgroup
+  const uint32_t b = blockIdx.x, per = f.a_tiles + f.e_tiles;
+  const uint32_t head = f.lag * f.a_tiles, mid = (f.n_groups - f.lag) * per;
+  uint32_t g, t;
+  bool amax_tile;
+  if (b < head) {
+    g = b / f.a_tiles;
+    t = b - g * f.a_tiles;
+    amax_tile = true;
+  } else if (b - head < mid) {
+    const uint32_t k = b - head, j = k / per, o = k - j * per;
+    amax_tile = o < f.a_tiles;
+    g = amax_tile ? f.lag + j : j;
+    t = amax_tile ? o : o - f.a_tiles;
+  } else {
+    const uint32_t k = b - head - mid, j = k / f.e_tiles;
+    g = f.n_groups - f.lag + j;
+    t = k - j * f.e_tiles;
+    amax_tile = false;
+  }
+  const int64_t gbeg = (int64_t)g * f.units_per_group;
+  const int64_t gend = min(gbeg + f.units_per_group, f.units_total);
+  uint32_t* const out = FAKE ? (uint32_t*)fake_y : codes;
+  uint32_t* const w_count = handoff_word<FAKE>(out, gbeg);
+  uint32_t* const w_max = handoff_word<FAKE>(out, gbeg + 32);
+  uint32_t* const w_ready = handoff_word<FAKE>(out, gbeg + 64);
+  __shared__ uint32_t red[THREADS / 64];
+  __shared__ uint32_t ready_bits;
+
+  if (amax_tile) {
+    const int64_t beg = gbeg + (int64_t)t * kAppendATile;
+    const int64_t end = min(beg + kAppendATile, gend);
+    const uint32_t m = workgroup_max<THREADS>(thread_absmax<THREADS>(x, beg, end), red);
+    if (threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_fetch_max(w_max, m << 16, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      // old >> 31 is 0 (a magnitude pattern << 16); using it orders the add after the max
+      const uint32_t done = __hip_atomic_fetch_add(w_count, 1u + (old >> 31), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (done + 1u == f.a_tiles) {
+        const uint32_t fin = __hip_atomic_load(w_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        amax_bits[g] = fin;
+        __hip_atomic_store(w_ready, fin | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+
+  if (threadIdx.x == 0) {
+    uint32_t c = __hip_atomic_load(w_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!(c & 1u) && f.wait_ticks > 0) {
+      const uint64_t t0 = wall_clock64();
+      do {
+        __builtin_amdgcn_s_sleep(8);
+        c = __hip_atomic_load(w_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while (!(c & 1u) && wall_clock64() - t0 < f.wait_ticks);
+    }
+    ready_bits = c;
+  }
+  __syncthreads();
+  uint32_t abits = ready_bits;  // uniform
+  if (abits & 1u)
+    abits &= 0xFFFF0000u;
+  else  // not published within the bound: the group max, computed here
+    abits = workgroup_max<THREADS>(thread_absmax<THREADS>(x, gbeg, gend), red) << 16;
+
+  const int64_t beg = gbeg + (int64_t)t * kAppendETile;
+  const int64_t end = min(beg + kAppendETile, gend);
+  const float A = __uint_as_float(abits);
+  const float s_enc = (A > 0.0f) ? kGlobalDiv / A : 0.0f;
+  __shared__ Tables tabs;
+  init_tables(&tabs, A / kGlobalDiv, THREADS);
+  constexpr int UNR = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t base = beg + wave * 64 * UNR; base < end; base += THREADS * UNR) {
+    uint4 v[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      v[k] = (u < end) ? x[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int64_t u = base + k * 64 + lane;
+      const Cand pick = encode_unit<RULE>(v[k], s_enc, &tabs);
+      const int64_t rel = u - gbeg;
+      const bool handoff = t == 0 && (rel == 0 || rel == 32 || rel == 64);
+      if (u < end) {
+        if constexpr (FAKE) {
+          if (!handoff) store_nt(fake_y + u, decode8(pick.codes, pick.S));
+        } else {
+          if (!handoff) __builtin_nontemporal_store(pick.codes, codes + u);
+          if ((lane & 1) == 0) scales[u >> 1] = (uint8_t)pick.sf;
+        }
+      }
+    }
+  }
+}
+
+// Units 0, 32 and 64 of each group (lanes 0..5 hold the blocks (0,1), (32,33), (64,65)),
+// after append_kernel: the same encode, stored over the hand-off words.  One wave per group.
+template <int RULE, bool FAKE>
+__global__ __launch_bounds__(64) void append_finish_kernel(const uint4* __restrict__ x,
+                                                           const float* __restrict__ amax,
+                                                           uint32_t* __restrict__ codes,
+                                                           uint4* __restrict__ fake_y,
+                                                           int64_t units_per_group) {
+  const int lane = threadIdx.x;
+  const int64_t u = (int64_t)blockIdx.x * units_per_group + (lane >> 1) * 32 + (lane & 1);
+  const bool active = lane < 6;
+  const uint4 v = active ? x[u] : make_uint4(0, 0, 0, 0);
+  const float A = amax[blockIdx.x];
+  const float s_enc = (A > 0.0f) ? kGlobalDiv / A : 0.0f;
+  __shared__ Tables tabs;
+  init_tables(&tabs, A / kGlobalDiv, 64);
+  const Cand pick = encode_unit<RULE>(v, s_enc, &tabs);
+  if (active && (lane & 1) == 0) {
+    if constexpr (FAKE)
+      store_nt(fake_y + u, decode8(pick.codes, pick.S));
+    else
+      codes[u] = pick.codes;
   }
 }
 
@@ -542,11 +765,106 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
   return launched();
 }
 
+// Process-wide options (kvfp4_set_option).
+std::atomic<int64_t> g_opt_append_fused{1};
+std::atomic<int64_t> g_opt_append_wait_us{20000};
+
+// Wall-clock ticks in `us` microseconds on the current device (its wall-clock rate is read
+// once per device; 100 MHz if the runtime does not report it).
+uint64_t wall_ticks(int64_t us) {
+  static std::atomic<int> khz_of[64];
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < 64) khz = khz_of[dev].load(std::memory_order_relaxed);
+  if (khz <= 0) {
+    if (dev < 0 || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+      khz = 100000;
+    if (dev >= 0 && dev < 64) khz_of[dev].store(khz, std::memory_order_relaxed);
+  }
+  return (uint64_t)us * (uint64_t)khz / 1000u;
+}
+
+// One-launch append (three launches: hand-off clear, append, finish) when it applies: no
+// block table, not in place, every group at least 66 units, grid within 32 bits.  Sets
+// *used; returns the status of what it enqueued.
+template <int RULE, int THREADS>
+int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
+                  uint8_t* codes, uint8_t* scales, float* group_amax, uint16_t* fake_y,
+                  hipStream_t s, bool* used) {
+  *used = false;
+  const int64_t upr = head_dim / 8;
+  const int64_t upg = (rpg < rows ? rpg : rows) * upr;
+  const int64_t ng = (rows - 1) / rpg + 1;
+  const int64_t total = rows * upr;
+  if (total - (ng - 1) * upg < 66) return KVFP4_OK;
+  const int64_t ta = (upg + kAppendATile - 1) / kAppendATile;
+  const int64_t te = (upg + kAppendETile - 1) / kAppendETile;
+  if (ng * (ta + te) > INT32_MAX) return KVFP4_OK;
+  int64_t lag = (kAppendLagUnits + upg - 1) / upg;
+  if (lag > ng) lag = ng;
+  const int64_t wait_us = g_opt_append_wait_us.load(std::memory_order_relaxed);
+  Append f;
+  f.units_total = total;
+  f.units_per_group = upg;
+  f.n_groups = (uint32_t)ng;
+  f.lag = (uint32_t)lag;
+  f.a_tiles = (uint32_t)ta;
+  f.e_tiles = (uint32_t)te;
+  f.wait_ticks = wait_us > 0 ? wall_ticks(wait_us) : 0;
+  *used = true;
+  uint32_t* out = fake_y ? (uint32_t*)fake_y : (uint32_t*)codes;
+  const int64_t cblocks = (3 * ng + 255) / 256;
+  const unsigned cgrid = (unsigned)(cblocks < 1024 ? cblocks : 1024);
+  hipLaunchKernelGGL(append_clear_kernel, dim3(cgrid), dim3(256), 0, s, out, upg, ng,
+                     fake_y ? 4 : 1);
+  int rc = launched();
+  if (rc != KVFP4_OK) return rc;
+  const unsigned grid = (unsigned)(ng * (ta + te));
+  if (fake_y) {
+    hipLaunchKernelGGL((append_kernel<RULE, THREADS, true>), dim3(grid), dim3(THREADS), 0, s,
+                       (const uint4*)x, (uint32_t*)group_amax, nullptr, nullptr, (uint4*)fake_y, f);
+    if ((rc = launched()) != KVFP4_OK) return rc;
+    hipLaunchKernelGGL((append_finish_kernel<RULE, true>), dim3((unsigned)ng), dim3(64), 0, s,
+                       (const uint4*)x, group_amax, nullptr, (uint4*)fake_y, upg);
+  } else {
+    hipLaunchKernelGGL((append_kernel<RULE, THREADS, false>), dim3(grid), dim3(THREADS), 0, s,
+                       (const uint4*)x, (uint32_t*)group_amax, (uint32_t*)codes, scales, nullptr,
+                       f);
+    if ((rc = launched()) != KVFP4_OK) return rc;
+    hipLaunchKernelGGL((append_finish_kernel<RULE, false>), dim3((unsigned)ng), dim3(64), 0, s,
+                       (const uint4*)x, group_amax, (uint32_t*)codes, nullptr, upg);
+  }
+  return launched();
+}
+
 // Shared body of the dense, paged and fake quantize entry points (arguments already
 // checked).  With fake_y set, the encode pass writes bf16 there instead of codes/scales.
+// Dense, not-in-place calls take the one-launch append where it applies (and the option
+// allows); the rest take three kernels: clear, group amax, encode.
 int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
                   float* group_amax, uint16_t* fake_y, hipStream_t s) {
+  if (!table && (const void*)fake_y != (const void*)x &&
+      g_opt_append_fused.load(std::memory_order_relaxed) != 0) {
+    bool used = false;
+    int arc;
+    switch (rule) {
+      case KVFP4_RULE_STATIC6:
+        arc = launch_append<KVFP4_RULE_STATIC6, kAppendStaticThreads>(
+            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+        break;
+      case KVFP4_RULE_STATIC4:
+        arc = launch_append<KVFP4_RULE_STATIC4, kAppendStaticThreads>(
+            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+        break;
+      default:
+        arc = launch_append<KVFP4_RULE_MSE, kAppendMseThreads>(
+            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+        break;
+    }
+    if (used) return arc;
+  }
   Part apart;
   unsigned agrid = 0;
   int rc = plan(rows, head_dim, rpg, tile_units(kAmaxThreads, kAmaxUnroll, kAmaxSteps), &apart,
@@ -806,5 +1124,34 @@ extern "C" const char* kvfp4_status_str(int status) {
 }
 
 extern "C" int kvfp4_abi_version(void) { return KVFP4_ABI_VERSION; }
+
+extern "C" int kvfp4_set_option(int32_t option, int64_t value) {
+  switch (option) {
+    case KVFP4_OPT_APPEND_FUSED:
+      if (value != 0 && value != 1) return KVFP4_EINVAL;
+      g_opt_append_fused.store(value, std::memory_order_relaxed);
+      return KVFP4_OK;
+    case KVFP4_OPT_APPEND_WAIT_US:
+      if (value < 0 || value > INT64_C(60000000)) return KVFP4_EINVAL;
+      g_opt_append_wait_us.store(value, std::memory_order_relaxed);
+      return KVFP4_OK;
+    default:
+      return KVFP4_EINVAL;
+  }
+}
+
+extern "C" int kvfp4_get_option(int32_t option, int64_t* value) {
+  if (!value) return KVFP4_EINVAL;
+  switch (option) {
+    case KVFP4_OPT_APPEND_FUSED:
+      *value = g_opt_append_fused.load(std::memory_order_relaxed);
+      return KVFP4_OK;
+    case KVFP4_OPT_APPEND_WAIT_US:
+      *value = g_opt_append_wait_us.load(std::memory_order_relaxed);
+      return KVFP4_OK;
+    default:
+      return KVFP4_EINVAL;
+  }
+}
 
 extern "C" int kvfp4_last_hip_error(void) { return g_last_hip_error; }

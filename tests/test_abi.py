@@ -241,3 +241,30 @@ def test_f32_and_fake_zero_rows_are_noops():
     assert dqf(rows=0, codes=None, scales=None, amax=None, y=None) == KVFP4_OK
     assert dqpf(nb=0, codes=None, scales=None, amax=None, tab=None, y=None) == KVFP4_OK
     assert fq(rows=0, x=None, amax=None, y=None) == KVFP4_OK
+
+
+def test_options_set_get_and_reject():
+    """The two process-wide options: defaults, round trip, rejected values (host only)."""
+    import ctypes
+
+    import kv_cache_fp4_amd as kv
+    L = kv.lib
+    v = ctypes.c_int64()
+    assert L.kvfp4_get_option(1, ctypes.byref(v)) == 0 and v.value in (0, 1)
+    saved_fused = v.value
+    assert L.kvfp4_get_option(2, ctypes.byref(v)) == 0 and v.value >= 0
+    saved_wait = v.value
+    try:
+        for opt, good, bad in ((1, (0, 1), (-1, 2, 7)), (2, (0, 1, 20000, 60000000), (-1, 60000001))):
+            for g in good:
+                assert L.kvfp4_set_option(opt, g) == 0
+                assert L.kvfp4_get_option(opt, ctypes.byref(v)) == 0 and v.value == g
+            for b in bad:
+                assert L.kvfp4_set_option(opt, b) == 1
+                assert L.kvfp4_get_option(opt, ctypes.byref(v)) == 0 and v.value == good[-1]
+        assert L.kvfp4_set_option(0, 1) == 1 and L.kvfp4_set_option(3, 1) == 1
+        assert L.kvfp4_get_option(3, ctypes.byref(v)) == 1
+        assert L.kvfp4_get_option(1, None) == 1
+    finally:
+        L.kvfp4_set_option(1, saved_fused)
+        L.kvfp4_set_option(2, saved_wait)
