@@ -470,6 +470,15 @@ def main(argv=None):
                                   w.rpg, y=w.out[r0:r1])
     ms_pl = _time_calls(per_layer, dev, max(args.steps // 3, 3), 2)
 
+    # The append again in the three-kernel form (clear, group amax, encode) for comparison
+    # with the one-kernel form the step used.
+    fused_before = w.kv.kvfp4_get_option("append_fused")
+    w.kv.kvfp4_set_option("append_fused", 0)
+    try:
+        ms_ap3 = _time_calls(w.append, dev, max(args.steps, 3), 2)
+    finally:
+        w.kv.kvfp4_set_option("append_fused", fused_before)
+
     step_bytes = w.append_bytes() + w.dequant_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     dq_gbs = w.dequant_bytes() / (ms_dq * 1e-3) / 1e9
@@ -506,6 +515,8 @@ def main(argv=None):
                      "bytes_per_launch": w.dequant_bytes(), "ms_per_launch": round(ms_dq, 4)},
         "breakdown": {"append_ms": round(ms_ap, 4), "append_GBps": round(ap_gbs, 2),
                       "append_bytes": w.append_bytes(),
+                      "append_form": "one-kernel" if fused_before else "three-kernel",
+                      "append_three_kernel_ms": round(ms_ap3, 4),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
         "per_layer_dequant": {"launches": n_launch, "ms_total": round(ms_pl, 4),
                               "us_per_launch": round(1e3 * ms_pl / n_launch, 2),

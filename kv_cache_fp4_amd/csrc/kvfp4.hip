@@ -20,10 +20,14 @@
 // store covers 64 consecutive units, so every wave instruction touches one contiguous
 // span (1 KiB of bf16, 256 B of codes).  Index math is 64-bit.
 //
-// Quantize ([P-NVFP4] "Stage 1"): (1) clear the group amax words, (2) group amax as a max
-// over 15-bit bf16 magnitude patterns with one atomicMax per workgroup, (3) encode: the two
-// lanes holding the halves of a 16-element block exchange half-block maxima through DPP,
-// both derive the same E4M3 scale, and each packs its 8 codes into one dword.
+// Quantize ([P-NVFP4] "Stage 1"): the group amax is a max over 15-bit bf16 magnitude
+// patterns; the encode has the two lanes holding the halves of a 16-element block exchange
+// half-block maxima through DPP, derive the same E4M3 scale, and each pack its 8 codes into
+// one dword.  Two forms with identical output: one kernel that does both for a whole chunk
+// (amax tiles hand each group's amax to its encode tiles through words in the group's own
+// output; see "one-launch append" below), and three kernels (clear the amax words, amax
+// pass with one atomicMax per workgroup, encode pass) for paged, in-place and tiny-group
+// calls.
 // Dequantize ([P-NVFP4] "Stage 3"): one pass; each lane turns one code dword and one scale
 // byte into 8 bf16 (one 16 B non-temporal store).
 #include <hip/hip_runtime.h>
