@@ -140,3 +140,28 @@ def test_append_into_cache_slab_both_forms_agree(options):
     assert np.array_equal(out[1][0].numpy(), oc)
     assert np.array_equal(out[1][1].numpy(), os_)
     assert np.array_equal(out[1][2].numpy().view(np.uint32), oa.view(np.uint32))
+
+
+def test_concurrent_appends_on_two_streams(options):
+    """Two one-kernel appends enqueued back to back on two streams, so that they can run at
+    the same time (different inputs and outputs): each call's hand-off lives in its own
+    output, so both match the oracle."""
+    kv = options
+    kv.kvfp4_set_option("append_fused", 1)
+    rows, d, rpg = 60000, 128, 6000
+    xs = [_x(rows, d, 100 + i) for i in range(2)]
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+    xd = [x.to(DEV) for x in xs]
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outs = []
+        for x, st in zip(xd, streams):
+            with torch.cuda.stream(st):
+                outs.append(kv.kvfp4_quantize(x, rpg, "mse", stream=st))
+        torch.cuda.synchronize()
+    for x, (c, s, a) in zip(xs, outs):
+        oc, os_, oa = oracle.quantize(_u16(x), rpg, "mse")
+        assert np.array_equal(c.cpu().numpy(), oc)
+        assert np.array_equal(s.cpu().numpy(), os_)
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), oa.view(np.uint32))
