@@ -206,9 +206,11 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
       const uint32_t* w1 = &w[1].x;
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {  // d = 8 j + 2 i2 and 8 j + 2 i2 + 1
-        *(uint32_t*)(v_buf + (8 * j + 2 * i2) * S::VSTR + pos) = (w0[i2] & 0xFFFFu) | (w1[i2] << 16);
+        // low halves of (w0, w1) and high halves: one byte permute each
+        *(uint32_t*)(v_buf + (8 * j + 2 * i2) * S::VSTR + pos) =
+            __builtin_amdgcn_perm(w1[i2], w0[i2], 0x05040100u);
         *(uint32_t*)(v_buf + (8 * j + 2 * i2 + 1) * S::VSTR + pos) =
-            (w0[i2] >> 16) | (w1[i2] & 0xFFFF0000u);
+            __builtin_amdgcn_perm(w1[i2], w0[i2], 0x07060302u);
       }
     }
   }
