@@ -44,7 +44,7 @@ namespace {
 // Launch shapes (threads per workgroup, units per lane per step, steps per workgroup),
 // chosen by sweeping on MI355X over the 30-layer cache shapes.
 constexpr int kAmaxThreads = 512, kAmaxUnroll = 4, kAmaxSteps = 4;
-constexpr int kQuantThreads = 128, kQuantUnroll = 2, kQuantSteps = 1;  // static rules
+constexpr int kQuantThreads = 128, kQuantUnroll = 2, kQuantSteps = 1;  // static rules, RTN
 constexpr int kMseThreads = 256, kMseUnroll = 2, kMseSteps = 4;        // mse rule
 constexpr int kDqThreads = 128, kDqUnroll = 2;                         // one step
 constexpr int kDqPagedThreads = 512;  // paged gather: one page lookup per 1024 units
