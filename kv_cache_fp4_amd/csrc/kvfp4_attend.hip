@@ -23,9 +23,10 @@
 //     ends up owning one query (column) and 32 of the 64 keys of the step; the other 32
 //     keys of that query sit in lane l ^ 32, and one exchange combines the two halves
 //     (of the final row sum, and of the row max on the rare steps that move it);
-//   - O^T = V^T P^T: B = P^T comes straight from the S^T registers (rounded to bf16), A =
-//     V^T read from LDS, where V is stored transposed with bits 2 and 3 of the key index
-//     swapped inside each 16-key block so that the 8 keys a lane needs are contiguous;
+//   - O^T = V^T P^T: B = P^T comes straight from the S^T registers (rounded to bf16), so a
+//     lane's 8 k values are the keys {0..3, 8..11} + 4 (l / 32) of a 16-key block; A = V^T
+//     with the same keys, gathered from the row-major V tile in LDS by two transposing
+//     reads (ds_read_b64_tr_b16, 4 keys each);
 //   - O^T's columns are queries again, so the softmax rescale is lane-local.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -38,6 +39,9 @@ namespace kvfp4 {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -53,15 +57,12 @@ struct AttShape {
   static constexpr int DB = D / 32;       // 32-row d blocks of O^T
   static constexpr int UPR = D / 8;       // code dwords per row
   static constexpr int KSTR = D + 8;      // K tile row stride in bf16 (16 B pad: no bank clash)
-  static constexpr int VSTR = kAtBN + 8;  // V^T tile row stride in bf16
+  static constexpr int VSTR = 144;        // V tile row stride in bf16 (72 dwords: the 4 rows a
+                                          // transposing read touches fall in distinct banks)
 };
 
-// Position of key r (0..15) inside its 16-key block of the V^T tile: bits 2 and 3 swapped.
-__device__ __forceinline__ int vperm(int r) { return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Per-thread share of one 64-key step.  K: KU units (u = tid + kAtThreads r: key u / UPR,
-// d-chunk u % UPR).  V: VU pairs of consecutive keys of one d-chunk (p = tid + kAtThreads r:
-// d-chunk p / 32, keys 2 (p % 32) and 2 (p % 32) + 1).  Offsets are byte offsets from the
+// Per-thread share of one 64-key step: KU units of K and the same units of V (u = tid +
+// kAtThreads r: key u / UPR, d-chunk u % UPR).  Offsets are byte offsets from the
 // step's first row and are the same for every step (32-bit, so the loads take a uniform
 // 64-bit base plus a per-lane 32-bit offset).  KEXACT / VEXACT: every thread has all its
 // units (no idle lanes), so full steps need no per-lane predicate.
@@ -69,17 +70,14 @@ template <int D>
 struct Share {
   static constexpr int UPR = D / 8;
   static constexpr int KU = (kAtBN * UPR + kAtThreads - 1) / kAtThreads;
-  static constexpr int VU = ((kAtBN / 2) * UPR + kAtThreads - 1) / kAtThreads;
+  static constexpr int VU = KU;
   static constexpr bool KEXACT = (kAtBN * UPR) % kAtThreads == 0;
-  static constexpr bool VEXACT = ((kAtBN / 2) * UPR) % kAtThreads == 0;
+  static constexpr bool VEXACT = KEXACT;
   int kkey[KU];            // key index in the step (>= kAtBN: no unit)
   int kj[KU];              // d-chunk
   uint32_t kb[KU];         // code byte offset
   uint32_t ksb[KU];        // scale byte offset
-  int vkey[VU];            // first key of the pair (>= kAtBN: no pair)
-  int vj[VU];              // d-chunk
-  uint32_t vb[VU][2];
-  uint32_t vsb[VU][2];
+
 };
 
 template <int D>
@@ -97,27 +95,13 @@ __device__ __forceinline__ void make_share(Share<D>& sh, int H, int head) {
     sh.kb[r] = (row * Sh::UPR + j) * 4u;
     sh.ksb[r] = row * (D / 16) + (j >> 1);
   }
-#pragma unroll
-  for (int r = 0; r < Sh::VU; ++r) {
-    const int pi = tid + kAtThreads * r;
-    const bool ok = pi < (kAtBN / 2) * Sh::UPR;
-    const int j = ok ? pi / (kAtBN / 2) : 0, kp = pi % (kAtBN / 2);
-    sh.vkey[r] = ok ? 2 * kp : kAtBN;
-    sh.vj[r] = j;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t row = (uint32_t)((2 * kp + kk) * H + head);
-      sh.vb[r][kk] = (row * Sh::UPR + j) * 4u;
-      sh.vsb[r][kk] = row * (D / 16) + (j >> 1);
-    }
-  }
 }
 
 // Packed K/V data of one step held in registers between its load and its dequantization.
 template <int D>
 struct Raw {
   uint32_t kc[Share<D>::KU], ks[Share<D>::KU];
-  uint32_t vc[Share<D>::VU][2], vs[Share<D>::VU][2];
+  uint32_t vc[Share<D>::VU], vs[Share<D>::VU];
 };
 
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts: 32-bit data
@@ -153,12 +137,10 @@ __device__ __forceinline__ void load_raw(Raw<D>& r, const Share<D>& sh, int64_t 
     r.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(ks, (int)sh.ksb[i], 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < Sh::VU; ++i)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      r.vc[i][kk] = __builtin_amdgcn_raw_buffer_load_b32(vc, (int)sh.vb[i][kk], 0, 0);
-      r.vs[i][kk] = __builtin_amdgcn_raw_buffer_load_b8(vs, (int)sh.vsb[i][kk], 0, 0);
-    }
+  for (int i = 0; i < Sh::VU; ++i) {  // V units at the same offsets as K's
+    r.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(vc, (int)sh.kb[i], 0, 0);
+    r.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(vs, (int)sh.ksb[i], 0, 0);
+  }
 }
 
 // Group decode scales (A/2688) of the keys of one step.  With groups of at least kAtBN
@@ -169,9 +151,8 @@ struct StepScales {
   int split;
 };
 
-// Dequantize the step held in `raw` (first key t0) into one LDS buffer pair: K row-major
-// [key][d] (16 B per unit), V transposed [d][key'] with key' in vperm order inside 16-key
-// blocks, two keys per 4-byte write (vperm keeps pairs together).
+// Dequantize the step held in `raw` (first key t0) into one LDS buffer pair, K and V both
+// row-major [key][d] (one 16 B store per unit).
 template <int D, bool SHORT>
 __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh, int64_t t0,
                                            const StepScales& sc, int64_t tpg, int64_t n_groups,
@@ -191,27 +172,12 @@ __device__ __forceinline__ void stage_tile(const Raw<D>& raw, const Share<D>& sh
   }
 #pragma unroll
   for (int i = 0; i < Share<D>::VU; ++i) {
-    const int key = sh.vkey[i];
+    const int key = sh.kkey[i];
     if (Share<D>::VEXACT || key < kAtBN) {
-      uint4 w[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float sd = key + kk < sc.split ? sc.vd0 : sc.vd1;
-        if constexpr (SHORT) sd = vamax[min((t0 + key + kk) / tpg, n_groups - 1)] / kGlobalDiv;
-        w[kk] = decode8(raw.vc[i][kk], e4m3_tab[raw.vs[i][kk]] * sd);
-      }
-      const int j = sh.vj[i];
-      const int pos = (key & ~15) | vperm(key & 15);
-      const uint32_t* w0 = &w[0].x;
-      const uint32_t* w1 = &w[1].x;
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {  // d = 8 j + 2 i2 and 8 j + 2 i2 + 1
-        // low halves of (w0, w1) and high halves: one byte permute each
-        *(uint32_t*)(v_buf + (8 * j + 2 * i2) * S::VSTR + pos) =
-            __builtin_amdgcn_perm(w1[i2], w0[i2], 0x05040100u);
-        *(uint32_t*)(v_buf + (8 * j + 2 * i2 + 1) * S::VSTR + pos) =
-            __builtin_amdgcn_perm(w1[i2], w0[i2], 0x07060302u);
-      }
+      float sd = key < sc.split ? sc.vd0 : sc.vd1;
+      if constexpr (SHORT) sd = vamax[min((t0 + key) / tpg, n_groups - 1)] / kGlobalDiv;
+      *(uint4*)(v_buf + key * S::VSTR + sh.kj[i] * 8) =
+          decode8(raw.vc[i], e4m3_tab[raw.vs[i]] * sd);
     }
   }
 }
@@ -273,12 +239,19 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     float qk_scale_log2, uint16_t* __restrict__ out) {
   using S = AttShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kAtBN * S::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][D * S::VSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kAtBN * S::VSTR];
 
   const int head = blockIdx.y;
   const int64_t q0 = (int64_t)blockIdx.x * kAtBM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  // Transposing LDS reads: within each 16-lane group, lane r addresses row (key) r / 4 and
+  // columns (d) 4 (r % 4) .. +3 of a 4 x 16 block and receives column r of it (checked on
+  // the device: lane i gets element i % 4 of the chunks addressed by lanes 4k + i / 4).
+  // Group g = lane / 16 covers d 16 (g % 2) .. +15 and keys 4 (g / 2) .. +3; the second read
+  // takes the keys 8 further on.
+  const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Q^T operands: query q0 + 32*wave + l32, d = 16*kc + 8*hh .. +7.
   const int64_t qrow = q0 + wave * kAtWaveQ + l32;
@@ -413,8 +386,14 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int db = 0; db < S::DB; ++db) {
-          const bf16x8 a = *(const bf16x8*)(vb + (32 * db + l32) * S::VSTR + 32 * rb +
-                                            16 * s2 + 8 * hh);
+          // A = V^T rows d = 32 db + l32, keys 32 rb + 16 s2 + 4 hh + {0..3, 8..11}, from
+          // the row-major V tile by two transposing reads (4 keys each).
+          const __bf16* p = vb + (32 * rb + 16 * s2 + tr_key) * S::VSTR + 32 * db + tr_d;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+          const v4i16 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * S::VSTR));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3],
+                                                              hi[0], hi[1], hi[2], hi[3]});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][s2], o[db], 0, 0, 0);
         }
       }
