@@ -18,7 +18,9 @@
 // Mapping (v_mfma_f32_32x32x16_bf16; a lane holds 8 consecutive k of one row of A and of
 // one column of B; accumulator register j of lane l is row 8*(j/4) + 4*(l/32) + j%4,
 // column l%32):
-//   - a workgroup is 8 waves x 32 queries of one head; a step covers 64 keys;
+//   - a workgroup is 8 MFMA waves x 32 queries of one head plus 4 staging waves (one per
+//     SIMD) that only dequantize K/V into LDS, so each SIMD always has vector work to issue
+//     beside its two MFMA waves; a step covers 64 keys;
 //   - S^T = K Q^T: A = K rows from LDS, B = the wave's Q^T held in registers, so each lane
 //     ends up owning one query (column) and 32 of the 64 keys of the step; the other 32
 //     keys of that query sit in lane l ^ 32, and one exchange combines the two halves
@@ -45,8 +47,10 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-constexpr int kAtWaves = 8;                  // waves per workgroup (2 per SIMD)
-constexpr int kAtThreads = 64 * kAtWaves;
+constexpr int kAtWaves = 8;                  // MFMA + softmax waves per workgroup
+constexpr int kAtProdWaves = 4;              // K/V staging waves per workgroup (one per SIMD)
+constexpr int kAtThreads = 64 * (kAtWaves + kAtProdWaves);
+constexpr int kAtStage = 64 * kAtProdWaves;  // staging threads
 constexpr int kAtWaveQ = 32;                 // queries per wave
 constexpr int kAtBM = kAtWaveQ * kAtWaves;   // queries per workgroup
 constexpr int kAtBN = 64;                    // keys per step
@@ -61,17 +65,17 @@ struct AttShape {
                                           // transposing read touches fall in distinct banks)
 };
 
-// Per-thread share of one 64-key step: KU units of K and the same units of V (u = tid +
-// kAtThreads r: key u / UPR, d-chunk u % UPR).  Offsets are byte offsets from the
+// Per-thread share of one 64-key step among the staging threads (t = 0 .. kAtStage-1): KU
+// units of K and the same units of V (u = t + kAtStage r: key u / UPR, d-chunk u % UPR).  Offsets are byte offsets from the
 // step's first row and are the same for every step (32-bit, so the loads take a uniform
 // 64-bit base plus a per-lane 32-bit offset).  KEXACT / VEXACT: every thread has all its
 // units (no idle lanes), so full steps need no per-lane predicate.
 template <int D>
 struct Share {
   static constexpr int UPR = D / 8;
-  static constexpr int KU = (kAtBN * UPR + kAtThreads - 1) / kAtThreads;
+  static constexpr int KU = (kAtBN * UPR + kAtStage - 1) / kAtStage;
   static constexpr int VU = KU;
-  static constexpr bool KEXACT = (kAtBN * UPR) % kAtThreads == 0;
+  static constexpr bool KEXACT = (kAtBN * UPR) % kAtStage == 0;
   static constexpr bool VEXACT = KEXACT;
   int kkey[KU];            // key index in the step (>= kAtBN: no unit)
   int kj[KU];              // d-chunk
@@ -83,10 +87,10 @@ struct Share {
 template <int D>
 __device__ __forceinline__ void make_share(Share<D>& sh, int H, int head) {
   using Sh = Share<D>;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x - 64 * kAtWaves;
 #pragma unroll
   for (int r = 0; r < Sh::KU; ++r) {
-    const int ui = tid + kAtThreads * r;
+    const int ui = tid + kAtStage * r;
     const int key = ui < kAtBN * Sh::UPR ? ui / Sh::UPR : kAtBN;
     const int j = ui % Sh::UPR;
     sh.kkey[r] = key;
@@ -226,10 +230,10 @@ __device__ __forceinline__ StepScales step_scales(GroupCursor& gc, int64_t t0, i
   return sc;
 }
 
-// Software pipeline over 64-key steps with two LDS buffers: while step i runs its MFMAs on
-// buffer i%2, the packed data of step i+1 (loaded into registers one step earlier) is
-// dequantized into the other buffer and the loads for step i+2 are issued; one barrier per
-// step.
+// Software pipeline over 64-key steps with two LDS buffers: while the MFMA waves run step i
+// on buffer i%2, the staging waves dequantize step i+1 (loaded into their registers one step
+// earlier) into the other buffer and issue the loads of step i+2; one barrier per step,
+// which every wave of both kinds executes.
 template <int D, bool SHORT>
 __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
     const uint16_t* __restrict__ q, int64_t Tq, const uint32_t* __restrict__ kcodes,
@@ -253,6 +257,44 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // The 127 E4M3 scale values (exact), looked up instead of decoded per unit.
+  __shared__ float e4m3_tab[128];
+  if (tid < 128) e4m3_tab[tid] = e4m3_decode((uint32_t)tid);
+  __syncthreads();
+
+  if (wave >= kAtWaves) {
+    // Staging waves: dequantize each step into the buffer the MFMA waves read next; one
+    // barrier per step, as the MFMA waves.
+    Share<D> sh;
+    make_share<D>(sh, H, head);
+    GroupCursor gc;
+    gc.g = 0;
+    gc.bnd = tpg;
+    if constexpr (!SHORT) cursor_load(gc, n_groups, kamax, vamax);
+    Raw<D> raw;
+    const auto keys_in = [&](int64_t t) {
+      return (int)(Tk - t >= kAtBN ? kAtBN : (Tk - t > 0 ? Tk - t : 0));
+    };
+    const auto load = [&](int64_t t) {
+      load_raw<D>(raw, sh, t, keys_in(t), H, kcodes, kscales, vcodes, vscales);
+    };
+    load(0);
+    stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax),
+                         tpg, n_groups, kamax, vamax, k_lds[0], v_lds[0], e4m3_tab);
+    load(kAtBN);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN, buf ^= 1) {
+      const int64_t t1 = t0 + kAtBN;
+      const StepScales sc = step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax);
+      stage_tile<D, SHORT>(raw, sh, t1, sc, tpg, n_groups, kamax, vamax, k_lds[buf ^ 1],
+                           v_lds[buf ^ 1], e4m3_tab);
+      load(t1 + kAtBN);
+      __syncthreads();
+    }
+    return;
+  }
+
   // Q^T operands: query q0 + 32*wave + l32, d = 16*kc + 8*hh .. +7.
   const int64_t qrow = q0 + wave * kAtWaveQ + l32;
   bf16x8 qb[S::KCH];
@@ -273,36 +315,12 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   // exceed 2^8, so most steps skip the rescale of O.
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // The 127 E4M3 scale values (exact), looked up instead of decoded per unit.
-  __shared__ float e4m3_tab[128];
-  if (tid < 128) e4m3_tab[tid] = e4m3_decode((uint32_t)tid);
-  __syncthreads();
-  Share<D> sh;
-  make_share<D>(sh, H, head);
-  GroupCursor gc;
-  gc.g = 0;
-  gc.bnd = tpg;
-  if constexpr (!SHORT) cursor_load(gc, n_groups, kamax, vamax);
-  Raw<D> raw;
-  // Keys of the step starting at t (0 past the end: its loads read nothing).
-  const auto keys_in = [&](int64_t t) {
-    return (int)(Tk - t >= kAtBN ? kAtBN : (Tk - t > 0 ? Tk - t : 0));
-  };
-  const auto load = [&](int64_t t) {
-    load_raw<D>(raw, sh, t, keys_in(t), H, kcodes, kscales, vcodes, vscales);
-  };
-  load(0);
-  stage_tile<D, SHORT>(raw, sh, 0, step_scales<SHORT>(gc, 0, tpg, n_groups, kamax, vamax), tpg,
-                       n_groups, kamax, vamax, k_lds[0], v_lds[0], e4m3_tab);
-  load(kAtBN);
-  __syncthreads();
+  __syncthreads();  // step 0 staged
 
   int buf = 0;
   for (int64_t t0 = 0; t0 < Tk; t0 += kAtBN, buf ^= 1) {
     const __bf16* kb = k_lds[buf];
     const __bf16* vb = v_lds[buf];
-    const int64_t t1 = t0 + kAtBN;
-    const StepScales sc = step_scales<SHORT>(gc, t1, tpg, n_groups, kamax, vamax);
     // One basic block: S^T = K Q^T for 64 keys (two 32-key row blocks) x the wave's 32
     // queries; the next step dequantized into the other buffer (unconditionally: past the
     // end it stages zeros that nobody reads); the loads of the step after.
@@ -316,9 +334,6 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kc], s[rb], 0, 0, 0);
       }
     }
-    stage_tile<D, SHORT>(raw, sh, t1, sc, tpg, n_groups, kamax, vamax, k_lds[buf ^ 1],
-                         v_lds[buf ^ 1], e4m3_tab);
-    load(t1 + kAtBN);
 
     // Online softmax for query l32 in base 2: weights exp2(c s - m) with c = scale*log2(e)
     // > 0 and m the running max of c s.  Keys past Tk (last step only) are masked to -inf.
