@@ -546,9 +546,8 @@ __global__ __launch_bounds__(THREADS) void dequant_kernel(const uint32_t* __rest
 
 // float32 output ([P-NVFP4] "Stage 3": float32 or bf16).  A lane takes half a unit (4
 // elements: one 16-bit code load, one 16 B store), so each wave store still covers one
-// contiguous 1 KiB span; the slice is the same 256 units as the bf16 kernel.
-constexpr int kDqfThreads = 128, kDqfUnroll = 4;  // half units per lane
-static_assert(kDqfThreads * kDqfUnroll == 2 * kDqThreads * kDqUnroll, "same slice as bf16");
+// contiguous 1 KiB span; one step of 512 units per workgroup.
+constexpr int kDqfThreads = 256, kDqfUnroll = 4;  // half units per lane (measured)
 
 __global__ __launch_bounds__(kDqfThreads) void dequant_f32_kernel(const uint16_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ scales,
@@ -905,7 +904,9 @@ int dequantize_impl(const uint8_t* codes, const uint8_t* scales, const float* gr
   const int threads = (table && !y32) ? kDqPagedThreads : kDqThreads;
   Part part;
   unsigned grid = 0;
-  int rc = plan(rows, head_dim, rpg, tile_units(threads, kDqUnroll, 1), &part, &grid);
+  const int64_t slice =
+      y32 ? (int64_t)kDqfThreads * kDqfUnroll / 2 : tile_units(threads, kDqUnroll, 1);
+  int rc = plan(rows, head_dim, rpg, slice, &part, &grid);
   if (rc != KVFP4_OK) return rc;
   part.table = table;
   if (table) part.n_pages = n_pages;
