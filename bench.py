@@ -126,7 +126,8 @@ class CacheWorkload:
 
 class PagedWorkload:
     """Paged cache of 30 layers x K,V x 2048 pages of 16 tokens x 12 heads x 128 (static_6),
-    physical pages in a seeded random order; the timed call gathers every page to dense bf16."""
+    physical pages in a seeded random order; the timed calls gather every page to dense bf16
+    and quantize every block into its page."""
 
     def __init__(self, device):
         import numpy as np
@@ -179,6 +180,17 @@ def bench_paged(device, steps=20, warmup=3):
                         "(random physical order, static_6) to dense bf16"),
            "ms_per_call": round(ms, 4), "bytes_per_call": w.dequant_bytes(),
            "GBps": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    # Quantizing every block into its page (same bytes), in both quantize forms.
+    quant = lambda: w.kv.kvfp4_quantize_paged(w.src, w.table, w.rpp, w.codes, w.scales,  # noqa: E731
+                                              w.amax, "static_6")
+    fused_before = w.kv.kvfp4_get_option("append_fused")
+    try:
+        for fused, key in ((1, "quantize"), (0, "quantize_three_kernel")):
+            w.kv.kvfp4_set_option("append_fused", fused)
+            qms = _time_calls(quant, device, max(steps // 2, 3), 2)
+            res[key] = {"ms": round(qms, 4), "GBps": round(w.dequant_bytes() / (qms * 1e-3) / 1e9, 2)}
+    finally:
+        w.kv.kvfp4_set_option("append_fused", fused_before)
     del w
     torch.cuda.empty_cache()
     return res

@@ -332,7 +332,17 @@ struct Append {
   uint32_t n_groups, lag;        // lag: groups, in [1, n_groups]
   uint32_t a_tiles, e_tiles;     // per group
   uint64_t wait_ticks;
+  const int32_t* table;          // paged cache: dense group g lives in page table[g]; or null
+  int64_t n_pages;
 };
+
+// Packed-side group of dense group g (itself without a table), or -1 for a table entry
+// outside [0, n_pages): that block is skipped.
+__device__ __forceinline__ int64_t append_page(const int32_t* table, int64_t n_pages, int64_t g) {
+  if (!table) return g;
+  const int64_t pg = table[g];
+  return (pg >= 0 && pg < n_pages) ? pg : -1;
+}
 
 // Max of the 15-bit magnitude patterns over units [beg, end), per thread.
 template <int THREADS>
@@ -375,11 +385,14 @@ __device__ __forceinline__ uint32_t* handoff_word(uint32_t* out, int64_t unit) {
 
 __global__ __launch_bounds__(256) void append_clear_kernel(uint32_t* __restrict__ out,
                                                            int64_t units_per_group,
-                                                           int64_t n_groups, int stride) {
+                                                           int64_t n_groups, int stride,
+                                                           const int32_t* __restrict__ table,
+                                                           int64_t n_pages) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 3 * n_groups;
        i += (int64_t)gridDim.x * 256) {
     const int64_t g = i / 3, k = i - g * 3;
-    out[(g * units_per_group + 32 * k) * stride] = 0u;
+    const int64_t pg = append_page(table, n_pages, g);
+    if (pg >= 0) out[(pg * units_per_group + 32 * k) * stride] = 0u;
   }
 }
 
@@ -409,12 +422,15 @@ __global__ __launch_bounds__(THREADS) void append_kernel(const uint4* __restrict
     t = k - j * f.e_tiles;
     amax_tile = false;
   }
+  const int64_t page = append_page(f.table, f.n_pages, g);
+  if (page < 0) return;  // uniform: no such page, nothing to read or write
   const int64_t gbeg = (int64_t)g * f.units_per_group;
   const int64_t gend = min(gbeg + f.units_per_group, f.units_total);
+  const int64_t shift = (page - (int64_t)g) * f.units_per_group;  // packed = dense + shift
   uint32_t* const out = FAKE ? (uint32_t*)fake_y : codes;
-  uint32_t* const w_count = handoff_word<FAKE>(out, gbeg);
-  uint32_t* const w_max = handoff_word<FAKE>(out, gbeg + 32);
-  uint32_t* const w_ready = handoff_word<FAKE>(out, gbeg + 64);
+  uint32_t* const w_count = handoff_word<FAKE>(out, gbeg + shift);
+  uint32_t* const w_max = handoff_word<FAKE>(out, gbeg + shift + 32);
+  uint32_t* const w_ready = handoff_word<FAKE>(out, gbeg + shift + 64);
   __shared__ uint32_t red[THREADS / 64];
   __shared__ uint32_t ready_bits;
 
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(THREADS) void append_kernel(const uint4* __restrict
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (done + 1u == f.a_tiles) {
         const uint32_t fin = __hip_atomic_load(w_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        amax_bits[g] = fin;
+        amax_bits[page] = fin;
         __hip_atomic_store(w_ready, fin | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -480,8 +496,8 @@ __global__ __launch_bounds__(THREADS) void append_kernel(const uint4* __restrict
         if constexpr (FAKE) {
           if (!handoff) store_nt(fake_y + u, decode8(pick.codes, pick.S));
         } else {
-          if (!handoff) __builtin_nontemporal_store(pick.codes, codes + u);
-          if ((lane & 1) == 0) scales[u >> 1] = (uint8_t)pick.sf;
+          if (!handoff) __builtin_nontemporal_store(pick.codes, codes + u + shift);
+          if ((lane & 1) == 0) scales[(u + shift) >> 1] = (uint8_t)pick.sf;
         }
       }
     }
@@ -495,12 +511,18 @@ __global__ __launch_bounds__(64) void append_finish_kernel(const uint4* __restri
                                                            const float* __restrict__ amax,
                                                            uint32_t* __restrict__ codes,
                                                            uint4* __restrict__ fake_y,
-                                                           int64_t units_per_group) {
+                                                           int64_t units_per_group,
+                                                           const int32_t* __restrict__ table,
+                                                           int64_t n_pages) {
+  const int64_t page = append_page(table, n_pages, blockIdx.x);
+  if (page < 0) return;  // uniform
   const int lane = threadIdx.x;
-  const int64_t u = (int64_t)blockIdx.x * units_per_group + (lane >> 1) * 32 + (lane & 1);
+  const int64_t rel = (lane >> 1) * 32 + (lane & 1);
+  const int64_t u = (int64_t)blockIdx.x * units_per_group + rel;  // dense side (x)
+  const int64_t pu = page * units_per_group + rel;                // packed side
   const bool active = lane < 6;
   const uint4 v = active ? x[u] : make_uint4(0, 0, 0, 0);
-  const float A = amax[blockIdx.x];
+  const float A = amax[page];
   const float s_enc = (A > 0.0f) ? kGlobalDiv / A : 0.0f;
   __shared__ Tables tabs;
   init_tables(&tabs, A / kGlobalDiv, 64);
@@ -509,7 +531,7 @@ __global__ __launch_bounds__(64) void append_finish_kernel(const uint4* __restri
     if constexpr (FAKE)
       store_nt(fake_y + u, decode8(pick.codes, pick.S));
     else
-      codes[u] = pick.codes;
+      codes[pu] = pick.codes;
   }
 }
 
@@ -788,13 +810,13 @@ uint64_t wall_ticks(int64_t us) {
   return (uint64_t)us * (uint64_t)khz / 1000u;
 }
 
-// One-launch append (three launches: hand-off clear, append, finish) when it applies: no
-// block table, not in place, every group at least 66 units, grid within 32 bits.  Sets
-// *used; returns the status of what it enqueued.
+// One-launch append (three launches: hand-off clear, append, finish) when it applies: not in
+// place, every group at least 66 units, grid within 32 bits (with a block table, a group is
+// a page).  Sets *used; returns the status of what it enqueued.
 template <int RULE, int THREADS>
 int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
-                  uint8_t* codes, uint8_t* scales, float* group_amax, uint16_t* fake_y,
-                  hipStream_t s, bool* used) {
+                  const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
+                  float* group_amax, uint16_t* fake_y, hipStream_t s, bool* used) {
   *used = false;
   const int64_t upr = head_dim / 8;
   const int64_t upg = (rpg < rows ? rpg : rows) * upr;
@@ -815,12 +837,14 @@ int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
   f.a_tiles = (uint32_t)ta;
   f.e_tiles = (uint32_t)te;
   f.wait_ticks = wait_us > 0 ? wall_ticks(wait_us) : 0;
+  f.table = table;
+  f.n_pages = table ? n_pages : ng;
   *used = true;
   uint32_t* out = fake_y ? (uint32_t*)fake_y : (uint32_t*)codes;
   const int64_t cblocks = (3 * ng + 255) / 256;
   const unsigned cgrid = (unsigned)(cblocks < 1024 ? cblocks : 1024);
   hipLaunchKernelGGL(append_clear_kernel, dim3(cgrid), dim3(256), 0, s, out, upg, ng,
-                     fake_y ? 4 : 1);
+                     fake_y ? 4 : 1, table, f.n_pages);
   int rc = launched();
   if (rc != KVFP4_OK) return rc;
   const unsigned grid = (unsigned)(ng * (ta + te));
@@ -829,41 +853,43 @@ int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
                        (const uint4*)x, (uint32_t*)group_amax, nullptr, nullptr, (uint4*)fake_y, f);
     if ((rc = launched()) != KVFP4_OK) return rc;
     hipLaunchKernelGGL((append_finish_kernel<RULE, true>), dim3((unsigned)ng), dim3(64), 0, s,
-                       (const uint4*)x, group_amax, nullptr, (uint4*)fake_y, upg);
+                       (const uint4*)x, group_amax, nullptr, (uint4*)fake_y, upg, table,
+                       f.n_pages);
   } else {
     hipLaunchKernelGGL((append_kernel<RULE, THREADS, false>), dim3(grid), dim3(THREADS), 0, s,
                        (const uint4*)x, (uint32_t*)group_amax, (uint32_t*)codes, scales, nullptr,
                        f);
     if ((rc = launched()) != KVFP4_OK) return rc;
     hipLaunchKernelGGL((append_finish_kernel<RULE, false>), dim3((unsigned)ng), dim3(64), 0, s,
-                       (const uint4*)x, group_amax, (uint32_t*)codes, nullptr, upg);
+                       (const uint4*)x, group_amax, (uint32_t*)codes, nullptr, upg, table,
+                       f.n_pages);
   }
   return launched();
 }
 
 // Shared body of the dense, paged and fake quantize entry points (arguments already
 // checked).  With fake_y set, the encode pass writes bf16 there instead of codes/scales.
-// Dense, not-in-place calls take the one-launch append where it applies (and the option
-// allows); the rest take three kernels: clear, group amax, encode.
+// Not-in-place calls take the one-launch append where it applies (and the option allows);
+// the rest take three kernels: clear, group amax, encode.
 int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
                   float* group_amax, uint16_t* fake_y, hipStream_t s) {
-  if (!table && (const void*)fake_y != (const void*)x &&
+  if ((const void*)fake_y != (const void*)x &&
       g_opt_append_fused.load(std::memory_order_relaxed) != 0) {
     bool used = false;
     int arc;
     switch (rule) {
       case KVFP4_RULE_STATIC6:
         arc = launch_append<KVFP4_RULE_STATIC6, kAppendStaticThreads>(
-            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
         break;
       case KVFP4_RULE_STATIC4:
         arc = launch_append<KVFP4_RULE_STATIC4, kAppendStaticThreads>(
-            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
         break;
       default:
         arc = launch_append<KVFP4_RULE_MSE, kAppendMseThreads>(
-            x, rows, head_dim, rpg, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
         break;
     }
     if (used) return arc;

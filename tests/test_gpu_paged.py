@@ -1,6 +1,8 @@
 """GPU parity of the paged-cache entry points against the oracle (bit for bit): permuted
-block tables with spare pages, skipped entries, pages gathered twice, every rule, and a
-full-size paged cache (16-token pages, 12 heads, 128 dims) on sampled pages."""
+block tables with spare pages, skipped entries on both the write and the read side, pages
+gathered twice, every rule, both quantize forms (one kernel with the hand-off in each page;
+three kernels), and a full-size paged cache (16-token pages, 12 heads, 128 dims) on sampled
+pages."""
 import numpy as np
 import pytest
 import torch
@@ -16,10 +18,21 @@ def _u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("rule", ["static_6", "static_4", "mse"])
-@pytest.mark.parametrize("nb,rpp,d", [(37, 16 * 12, 128), (5, 64, 64), (200, 16 * 4, 256)])
-def test_paged_round_trip_matches_oracle(rule, nb, rpp, d):
+@pytest.fixture
+def fused_option():
     import kv_cache_fp4_amd as kv
+    saved = kv.kvfp4_get_option("append_fused")
+    yield kv
+    kv.kvfp4_set_option("append_fused", saved)
+
+
+@pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
+@pytest.mark.parametrize("rule", ["static_6", "static_4", "mse"])
+@pytest.mark.parametrize("nb,rpp,d", [(37, 16 * 12, 128), (5, 64, 64), (200, 16 * 4, 256),
+                                      (9, 1, 64)])
+def test_paged_round_trip_matches_oracle(fused_option, fused, rule, nb, rpp, d):
+    kv = fused_option
+    kv.kvfp4_set_option("append_fused", fused)
     npg = nb + 7
     x = synth.gauss_outliers((nb * rpp, d), seed=nb + rpp + d)
     tab = np.random.default_rng(nb).permutation(npg)[:nb].astype(np.int32)
@@ -38,6 +51,31 @@ def test_paged_round_trip_matches_oracle(rule, nb, rpp, d):
     assert np.array_equal(scales.cpu().numpy(), os_)
     assert np.array_equal(amax.cpu().numpy(), oa)
     assert np.array_equal(_u16(y), oracle.dequantize_paged(oc, os_, oa, tab, rpp))
+
+
+@pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
+def test_paged_quantize_skips_entries(fused_option, fused):
+    """Write-side table entries outside [0, n_pages) are skipped: their blocks write nothing
+    and every page not named keeps its old bytes."""
+    kv = fused_option
+    kv.kvfp4_set_option("append_fused", fused)
+    nb, rpp, d, npg = 6, 192, 128, 5
+    x = synth.gauss_outliers((nb * rpp, d), seed=11)
+    tab = np.array([3, -1, 0, npg + 2, 1, 4], dtype=np.int32)
+    codes = torch.full((npg, rpp, d // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((npg, rpp, d // 16), 0x33, dtype=torch.uint8, device=DEV)
+    amax = torch.full((npg,), -3.0, dtype=torch.float32, device=DEV)
+    kv.kvfp4_quantize_paged(x.to(DEV), torch.from_numpy(tab).to(DEV), rpp, codes, scales, amax,
+                            "mse")
+    torch.cuda.synchronize()
+    oc = np.full((npg, rpp, d // 2), 0x5A, np.uint8)
+    os_ = np.full((npg, rpp, d // 16), 0x33, np.uint8)
+    oa = np.full(npg, -3.0, np.float32)
+    oracle.quantize_paged(_u16(x), tab, rpp, npg, "mse", oc, os_, oa)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(amax.cpu().numpy(), oa)
+    assert np.all(oc[2] == 0x5A) and oa[2] == -3.0  # page 2 is named by no valid entry
 
 
 def test_paged_gather_skips_and_repeats():
