@@ -159,7 +159,9 @@ int kvfp4_attend(const uint16_t* q, int64_t q_tokens, const uint8_t* k_codes,
  * [b*rows_per_page, (b+1)*rows_per_page)); 16-byte aligned.
  *
  * kvfp4_quantize_paged: quantize the dense rows block by block into their pages (group amax
- * = the block's amax, stored in page_amax[page]).  Two blocks naming the same page race.
+ * = the block's amax, stored in page_amax[page]), with the same kernels as kvfp4_quantize
+ * (in the one-kernel form the hand-off words sit in each named page's codes).  Two blocks
+ * naming the same page race.
  * kvfp4_dequantize_paged: gather the listed pages into dense bf16 rows; a page may be named
  * more than once.  Same arithmetic, errors and stream rules as the unpaged calls.
  */
@@ -237,9 +239,10 @@ int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
 /*
  * Process-wide options, read when a call enqueues its work (work already enqueued or
  * captured in a graph keeps the values it was enqueued with).  Neither changes any output.
- *   KVFP4_OPT_APPEND_FUSED    1 (default): kvfp4_quantize and kvfp4_fake_quantize (not in
- *                             place) take the one-kernel amax + encode form where it
- *                             applies; 0: always the three-kernel form.
+ *   KVFP4_OPT_APPEND_FUSED    1 (default): kvfp4_quantize, kvfp4_quantize_paged and
+ *                             kvfp4_fake_quantize (not in place) take the one-kernel
+ *                             amax + encode form where it applies; 0: always the
+ *                             three-kernel form.
  *   KVFP4_OPT_APPEND_WAIT_US  in the one-kernel form, the longest time (microseconds) an
  *                             encode workgroup waits for its group amax before computing it
  *                             itself from the input; 0 = never wait; default 20000, at
