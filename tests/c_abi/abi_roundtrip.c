@@ -1,7 +1,7 @@
 /*
  * abi_roundtrip.c -- a plain C program that uses libkvfp4 through its C ABI alone:
  * hipMalloc'd device buffers, a HIP stream of its own, every scale rule, several group
- * layouts, and host-side argument errors.  Its outputs are compared byte for byte with the
+ * layouts, both quantize forms (KVFP4_OPT_APPEND_FUSED), and host-side argument errors.  Its outputs are compared byte for byte with the
  * oracle (test infrastructure, loaded as its own library).  Exit status 0 = all equal.
  *
  * Input: bf16 bit patterns drawn from a fixed-seed xorshift generator with the exponent
@@ -101,11 +101,17 @@ int main(void) {
   hipStream_t st;
   CHECK_HIP(hipStreamCreate(&st));
   int bad = 0;
-  for (int rule = 0; rule < 3; ++rule) {
-    bad |= run_case(1000, 128, 300, rule, st);
-    bad |= run_case(37, 64, 10, rule, st);
-    bad |= run_case(513, 256, 513, rule, st);
+  /* both quantize forms (the one-kernel form applies to the first and third layouts) */
+  for (int fused = 1; fused >= 0; --fused) {
+    if (kvfp4_set_option(KVFP4_OPT_APPEND_FUSED, fused) != KVFP4_OK) bad = 1;
+    printf("append form: %s\n", fused ? "one kernel where it applies" : "three kernels");
+    for (int rule = 0; rule < 3; ++rule) {
+      bad |= run_case(1000, 128, 300, rule, st);
+      bad |= run_case(37, 64, 10, rule, st);
+      bad |= run_case(513, 256, 513, rule, st);
+    }
   }
+  if (kvfp4_set_option(KVFP4_OPT_APPEND_FUSED, 1) != KVFP4_OK) bad = 1;
   /* host-side argument errors: nothing is enqueued */
   void* p;
   CHECK_HIP(hipMalloc(&p, 1 << 16));
@@ -113,8 +119,13 @@ int main(void) {
   int e1 = kvfp4_quantize((const uint16_t*)(b + 8), 4, 64, 4, 0, b + 4096, b + 8192, (float*)(b + 12288), st);
   int e2 = kvfp4_dequantize(b, b + 4096, (const float*)(b + 8192), 4, 96, 4, (uint16_t*)(b + 12288), st);
   int e3 = kvfp4_quantize((const uint16_t*)b, 4, 64, 4, 7, b + 4096, b + 8192, (float*)(b + 12288), st);
-  printf("errors: misaligned x -> %d, head_dim 96 -> %d, rule 7 -> %d\n", e1, e2, e3);
-  bad |= !(e1 == KVFP4_EALIGN && e2 == KVFP4_EUNSUPPORTED && e3 == KVFP4_EINVAL);
+  int64_t ov = -1;
+  int e4 = kvfp4_set_option(99, 0);
+  int e5 = kvfp4_get_option(KVFP4_OPT_APPEND_WAIT_US, &ov);
+  printf("errors: misaligned x -> %d, head_dim 96 -> %d, rule 7 -> %d, option 99 -> %d\n", e1,
+         e2, e3, e4);
+  bad |= !(e1 == KVFP4_EALIGN && e2 == KVFP4_EUNSUPPORTED && e3 == KVFP4_EINVAL &&
+           e4 == KVFP4_EINVAL && e5 == KVFP4_OK && ov >= 0);
   CHECK_HIP(hipFree(p));
   CHECK_HIP(hipStreamDestroy(st));
   printf("%s\n", bad ? "FAILED" : "OK");

@@ -1,6 +1,7 @@
 """The library used from plain C: tests/c_abi/abi_roundtrip.c (built by __graft_entry__.build())
 allocates device buffers with hipMalloc, runs quantize + dequantize on a stream of its own
-for every rule and three group layouts, compares every output byte with the oracle, and
+for every rule, three group layouts and both quantize forms, compares every output byte with
+the oracle, and
 checks host-side argument errors.  It runs as its own process (its own HIP runtime)."""
 import os
 import subprocess
@@ -18,4 +19,4 @@ def test_c_program_round_trip_matches_oracle():
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith("OK")
-    assert r.stdout.count("bit-exact") == 9
+    assert r.stdout.count("bit-exact") == 18  # 3 layouts x 3 rules x 2 quantize forms
