@@ -1,8 +1,8 @@
 """The library used from plain C: tests/c_abi/abi_roundtrip.c (built by __graft_entry__.build())
 allocates device buffers with hipMalloc, runs quantize + dequantize on a stream of its own
 for every rule, three group layouts and both quantize forms, compares every output byte with
-the oracle, and
-checks host-side argument errors.  It runs as its own process (its own HIP runtime)."""
+the oracle, and checks host-side argument errors.  It runs as its own process (its own HIP
+runtime)."""
 import os
 import subprocess
 
