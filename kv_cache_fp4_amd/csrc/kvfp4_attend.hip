@@ -61,8 +61,9 @@ struct AttShape {
   static constexpr int DB = D / 32;       // 32-row d blocks of O^T
   static constexpr int UPR = D / 8;       // code dwords per row
   static constexpr int KSTR = D + 8;      // K tile row stride in bf16 (16 B pad: no bank clash)
-  static constexpr int VSTR = 144;        // V tile row stride in bf16 (72 dwords: the 4 rows a
-                                          // transposing read touches fall in distinct banks)
+  static constexpr int VSTR = 160;        // V tile row stride in bf16 (80 dwords: the 4 rows x
+                                          // 64 B that 32 lanes of a transposing read touch
+                                          // start 16 banks apart, so no bank conflicts)
 };
 
 // Per-thread share of one 64-key step among the staging threads (t = 0 .. kAtStage-1): KU
