@@ -67,10 +67,11 @@ struct AttShape {
 };
 
 // Per-thread share of one 64-key step among the staging threads (t = 0 .. kAtStage-1): KU
-// units of K and the same units of V (u = t + kAtStage r: key u / UPR, d-chunk u % UPR).  Offsets are byte offsets from the
-// step's first row and are the same for every step (32-bit, so the loads take a uniform
-// 64-bit base plus a per-lane 32-bit offset).  KEXACT / VEXACT: every thread has all its
-// units (no idle lanes), so full steps need no per-lane predicate.
+// units of K and the same units of V (u = t + kAtStage r: key u / UPR, d-chunk u % UPR).
+// Offsets are byte offsets from the step's first row and are the same for every step
+// (32-bit, so the loads take a uniform 64-bit base plus a per-lane 32-bit offset).
+// KEXACT / VEXACT: every thread has all its units (no idle lanes), so full steps need no
+// per-lane predicate.
 template <int D>
 struct Share {
   static constexpr int UPR = D / 8;
@@ -82,7 +83,6 @@ struct Share {
   int kj[KU];              // d-chunk
   uint32_t kb[KU];         // code byte offset
   uint32_t ksb[KU];        // scale byte offset
-
 };
 
 template <int D>
@@ -258,9 +258,10 @@ __global__ __launch_bounds__(kAtThreads, 1) void attend_kernel(
   const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // The 127 E4M3 scale values (exact), looked up instead of decoded per unit.
-  __shared__ float e4m3_tab[128];
-  if (tid < 128) e4m3_tab[tid] = e4m3_decode((uint32_t)tid);
+  // Decoded values of all 256 scale bytes (the dequantizer's own decode; bytes above 0x7E are
+  // never written by the quantizers), looked up instead of decoded per unit.
+  __shared__ float e4m3_tab[256];
+  if (tid < 256) e4m3_tab[tid] = e4m3_decode((uint32_t)tid);
   __syncthreads();
 
   if (wave >= kAtWaves) {
