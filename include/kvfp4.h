@@ -25,6 +25,10 @@
  *   mse: both candidates; err = fma-chain of (x_i - E2M1(c_i)*S)^2 over elements 0..7 plus
  *        the chain over 8..15; the 4-max candidate wins only if its err is strictly lower.
  *   dequantize: y_i = bf16_rne(E2M1(c_i) * (E4M3(sf) * (A/2688)))
+ *   a product with a zero operand is zero, also where binary32 would form 0*inf = NaN (a
+ *   group amax below about 2^-119 overflows s_enc or inv): an all-zero block gets scale
+ *   byte 0x00, a zero element code 0x0 / 0x8 by its sign; nonzero x*inf saturates.
+ *   Inputs must be finite; every finite input is in the domain.
  *
  * Conventions for every entry point:
  *   - pointers are DEVICE pointers unless stated; the caller allocates and frees all of
@@ -211,7 +215,7 @@ int kvfp4_fake_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64
  *
  * Per 16-element block along head_dim: qmax = 2^(bits-1) - 1 (7 or 1), s = bf16_rne(m/qmax)
  * with m = max|x| (binary32 division), inv = s > 0 ? 1/s : 0, q = clamp(rne(x*inv), -qmax,
- * qmax) stored as a two's-complement bit field, element 8k+i at bits [bits*i, bits*(i+1)) of
+ * qmax) (q = 0 for x = +-0 also when inv = inf) stored as a two's-complement bit field, element 8k+i at bits [bits*i, bits*(i+1)) of
  * its 8-element group (INT4: element 2j in the low nibble of byte j; INT2: element 4j+k at
  * bits 2k of byte j); dequant = bf16_rne(q * s).  No group amax.  One 16-bit scale per 16
  * elements: 5 bits/element (INT4), 3 bits/element (INT2, the 5.33x of [P-SF] Tables 4-5).

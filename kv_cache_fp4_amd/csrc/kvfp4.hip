@@ -204,13 +204,24 @@ template <int DV>
 __device__ __forceinline__ Cand make_cand(const float xf[8], uint32_t mb, float s_enc,
                                           const Tables* tb) {
   Cand c;
-  const float u = block_t<DV>(mb, tb) * s_enc;
+  // A product with a zero operand is zero, also where binary32 would form 0 * inf = NaN:
+  // s_enc = +inf (group amax below 2688/FLT_MAX) meets an all-zero block, or inv = +inf
+  // (S below 1/FLT_MAX, which needs S >= 2^-9 s_dec < 2^-128, i.e. s_enc > 2^119) meets a
+  // zero element.  Both need s_enc > 2^100, a test that is uniform over the group, so
+  // ordinary groups skip the fix-up.  Nonzero operands keep x * inf = +-inf (saturating).
+  const bool tiny_group = s_enc > 0x1p100f;
+  float u = block_t<DV>(mb, tb) * s_enc;
+  if (__builtin_expect(tiny_group, 0)) u = (mb == 0u) ? 0.0f : u;
   c.sf = e4m3_encode(u);
   c.S = tb->S[c.sf];
   const float inv = tb->inv[c.sf];
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = xf[i] * inv;
+  if (__builtin_expect(tiny_group, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (xf[i] == 0.0f) ? xf[i] : y[i];
+  }
   c.codes = e2m1_encode8(y);
   return c;
 }
@@ -636,10 +647,18 @@ __global__ __launch_bounds__(kQuantThreads) void rtn_quant_kernel(const uint4* _
       const uint32_t sh = pack_bf16x2(sq, 0.0f) & 0xFFFFu;
       const float sv = __uint_as_float(sh << 16);
       const float inv = (sv > 0.0f) ? 1.0f / sv : 0.0f;
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = xf[i] * inv;
+      // inv = +inf (s below 1/FLT_MAX): a zero element gives q = 0, not rint(0 * inf) = NaN.
+      if (__builtin_expect(inv > 3.40282347e38f, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = (xf[i] == 0.0f) ? 0.0f : p[i];
+      }
       uint32_t w = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float qf = fminf(fmaxf(__builtin_rintf(xf[i] * inv), -kQmax), kQmax);
+        const float qf = fminf(fmaxf(__builtin_rintf(p[i]), -kQmax), kQmax);
         w |= ((uint32_t)(int)qf & ((1u << BITS) - 1)) << (BITS * i);
       }
       if (u < r.end) {

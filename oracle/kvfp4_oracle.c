@@ -27,6 +27,10 @@
  *   - one global amax per scale group (one appended chunk of K or of V);
  *   - s_dec = A/2688 and s_enc = 2688/A for every rule (2688 = e2m1_max * e4m3_max);
  *   - per-block reciprocal inv = 1/S, then y = x*inv per element;
+ *   - a product with a zero operand is zero, also where binary32 would form 0*inf = NaN
+ *     (s_enc = 2688/A overflows when A < 2688/FLT_MAX, inv = 1/S when S < 1/FLT_MAX): an
+ *     all-zero block gets u = 0 (scale byte 0x00), a zero element y = +-0 (its own sign),
+ *     a zero RTN element q = 0; nonzero operands keep x*inf = +-inf, which saturates;
  *   - element 2j goes in the low nibble, 2j+1 in the high nibble;
  *   - mse: squared error of the fp32 reconstruction, fma chains over each half
  *     block, 4-max chosen only when strictly better.
@@ -164,13 +168,13 @@ typedef struct {
 static void make_candidate(const float* xb, float m, float dv, float s_enc, float s_dec,
                            candidate_t* c) {
   float t = m / dv;
-  float u = t * s_enc;
+  float u = (t == 0.0f) ? 0.0f : t * s_enc; /* zero block: u = 0 even if s_enc = inf */
   c->sf = kvfp4_oracle_e4m3_encode(u);
   float S = (float)kvfp4_oracle_e4m3_value(c->sf) * s_dec;
   float inv = (S > 0.0f) ? 1.0f / S : 0.0f;
   c->S = S;
   for (int i = 0; i < 16; ++i) {
-    float y = xb[i] * inv;
+    float y = (xb[i] == 0.0f) ? xb[i] : xb[i] * inv; /* +-0 stays +-0 even if inv = inf */
     c->code[i] = kvfp4_oracle_e2m1_encode(y);
   }
 }
@@ -388,7 +392,8 @@ int kvfp4_oracle_dequantize_paged_f32(const uint8_t* codes, const uint8_t* scale
  * block_size=16, packed storage plus per-block scales; on read the quantized prefix is
  * dequantized and the bf16 recent tail copied back in).
  * Per 16-element block: qmax = 2^(bits-1) - 1; s = bf16(m / qmax) with m = max |x|;
- * inv = s > 0 ? 1/s : 0; q = clamp(nearest-even(x * inv), -qmax, qmax) in two's complement,
+ * inv = s > 0 ? 1/s : 0; q = clamp(nearest-even(x * inv), -qmax, qmax) in two's complement
+ * (q = 0 for a zero x, also when inv = inf),
  * element 2j (INT4) or 4j+k (INT2) in the lowest bits first; dequant = bf16(q * s).
  * ---------------------------------------------------------------------------------- */
 int kvfp4_oracle_rtn_quantize(const uint16_t* x, int64_t rows, int d, int bits, uint8_t* codes,
@@ -410,7 +415,7 @@ int kvfp4_oracle_rtn_quantize(const uint16_t* x, int64_t rows, int d, int bits, 
       float inv = (sv > 0.0f) ? 1.0f / sv : 0.0f;
       scales[r * nb + b] = sh;
       for (int i = 0; i < 16; ++i) {
-        float v = rintf(xb[i] * inv);
+        float v = (xb[i] == 0.0f) ? 0.0f : rintf(xb[i] * inv); /* 0 even if inv = inf */
         if (v > (float)qmax) v = (float)qmax;
         if (v < (float)-qmax) v = (float)-qmax;
         int q = (int)v;

@@ -44,7 +44,9 @@ MUTANTS = {
     "attention scale ignored": ("s *= scale;", "s *= 1.0;"),
     "paged uses block index as page": ("int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),",
                                        "pg = b; int rc = kvfp4_oracle_dequantize_rows(codes + pg * rows_per_page * (d / 2),"),
-    "rtn truncates": ("float v = rintf(xb[i] * inv);", "float v = truncf(xb[i] * inv);"),
+    "rtn truncates": ("? 0.0f : rintf(xb[i] * inv);", "? 0.0f : truncf(xb[i] * inv);"),
+    "zero element times inf": ("float y = (xb[i] == 0.0f) ? xb[i] : xb[i] * inv;",
+                               "float y = xb[i] * inv;"),
     "rtn qmax off by one": ("const int qmax = (1 << (bits - 1)) - 1;\n  const int per_byte = 8 / bits;\n  const int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int b = 0;",
                             "const int qmax = (1 << (bits - 1));\n  const int per_byte = 8 / bits;\n  const int nb = d / 16;\n  for (int64_t r = 0; r < rows; ++r) {\n    for (int b = 0;"),
     "rtn scale kept in fp32": ("uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);\n      float sv = kvfp4_oracle_bf16_to_float(sh);",

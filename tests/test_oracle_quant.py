@@ -8,7 +8,9 @@ What each test would catch if the oracle were wrong:
   - static invariants: a divisor swapped between static_6 and static_4;
   - mse brute force: a wrong error definition, a flipped comparison or a wrong tie rule;
   - group tests: a wrong group index or amax scope;
-  - exhaustive dequant: a wrong E2M1 or E4M3 decode entry or a wrong product order.
+  - exhaustive dequant: a wrong E2M1 or E4M3 decode entry or a wrong product order;
+  - zero times infinity: a NaN (or a sign taken from it) where a zero element or an all-zero
+    block meets an overflowed s_enc or inv.
 """
 import numpy as np
 import pytest
@@ -200,6 +202,22 @@ def test_underflowing_block_is_zero(rule):
     assert c[1] == 8 and np.all(np.delete(c, 1) == 0)
     y = oracle.dequantize(codes, scales, amax, 1)[0, 16:]
     assert y[1] == 0x8000 and np.all(np.delete(y, 1) == 0)
+
+
+@pytest.mark.parametrize("rule", ["static_6", "static_4", "mse"])
+def test_zero_times_infinity_is_zero(rule):
+    """A group whose amax is 2^-129 (bf16 pattern 0x0010 = 16 * 2^-133): s_enc = 2688 * 2^129
+    overflows to +inf, so a nonzero block gets u = inf -> scale byte 0x7E; S = 448 * A/2688
+    (about 2^-129/6, a float32 subnormal) has 1/S > FLT_MAX, so inv = +inf: nonzero elements
+    go to +-inf and saturate (code 7 | sign), zero elements stay +-0 (codes 0x0 / 0x8); the
+    all-zero second block gets u = 0 -> scale byte 0x00.  Derived by hand from the reading
+    that a product with a zero operand is zero (binary32 would give 0 * inf = NaN)."""
+    x = np.zeros((1, 32), dtype=np.uint16)
+    x[0, :5] = [0x0010, 0x0000, 0x8000, 0x0001, 0x8001]   # 2^-129, +0, -0, 2^-133, -2^-133
+    codes, scales, amax = oracle.quantize(x, 1, rule)
+    assert amax.view(np.uint32)[0] == 0x00100000
+    assert scales.tolist() == [[0x7E, 0x00]]
+    assert codes.tolist() == [[0x07, 0x78, 0x0F, 0, 0, 0, 0, 0] + [0] * 8]
 
 
 def test_groups_are_independent_and_ragged_tail():

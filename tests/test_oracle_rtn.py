@@ -49,6 +49,19 @@ def test_worked_example(name):
         assert y.reshape(-1).tolist() == [int(t, 16) for t in c["dequant_bf16"].split()]
 
 
+def test_zero_times_infinity_is_zero():
+    """INT4 block with max 7 * 2^-130 (bf16 pattern 0x0038): s = bf16(m/7) = 2^-130 (pattern
+    0x0008) and 1/s = 2^130 > FLT_MAX, so inv = +inf: nonzero elements go to +-inf and clamp
+    to +-7, zero elements (either sign) give q = 0.  Derived by hand from the reading that a
+    product with a zero operand is zero (binary32 would give rint(0 * inf) = NaN)."""
+    x = np.zeros((1, 16), dtype=np.uint16)
+    x[0, :5] = [0x0038, 0x0000, 0x8000, 0x0001, 0x8001]  # 7*2^-130, +-0, +-2^-133
+    codes, scales = oracle.rtn_quantize(x, 4)
+    assert scales.tolist() == [[0x0008]]
+    # q = 7, 0, 0, 7, -7 (0x9), then zeros; element 2j in the low nibble
+    assert codes.tolist() == [[0x07, 0x70, 0x09, 0, 0, 0, 0, 0]]
+
+
 def test_int2_compression_matches_the_study():
     vals = {}
     for line in open(os.path.join(GOLDEN_DIR, "rtn_compression.txt")):
