@@ -4,6 +4,8 @@ Quantize: every finite bf16 bit pattern (65,280 of them, 510 rows of 128) under 
 in both quantize forms (one kernel; three kernels), arranged as
   - patterns in order, one group per row: each row holds 128 consecutive patterns (part of
     one binade's mantissas, one sign), so every row sits at its own magnitude;
+  - patterns in order in groups of 8 rows (128 units, so the one-kernel form applies, also
+    to the first groups, whose amax is small enough for s_enc and inv to overflow);
   - a seeded permutation, one group per row: blocks that mix magnitudes over the whole bf16
     range, so underflowing elements sit next to the block maximum;
   - the same permutation in groups of 7 rows (ragged last group of 6);
@@ -41,6 +43,7 @@ def _arrangements():
     perm = p[np.random.default_rng(0).permutation(p.size)]
     return {
         "in_order/1": (p.reshape(-1, D), 1),
+        "in_order/8": (p.reshape(-1, D), 8),
         "permuted/1": (perm.reshape(-1, D), 1),
         "permuted/7": (perm.reshape(-1, D), 7),
         "in_order/all": (p.reshape(-1, D), 510),
