@@ -13,6 +13,9 @@ in both quantize forms (one kernel; three kernels), arranged as
 Checked: codes, scale bytes, group amax, the bf16 dequantization of the GPU's own packed
 output, and fake quantization.
 
+Paged: the patterns in order as logical blocks written into pages in a random order (pages
+of 1 and 6 rows, both forms), gathered back to bf16 and float32.
+
 RTN INT4 / INT2: every finite pattern in order and permuted; codes, bf16 scales and the
 dequantization.
 
@@ -87,6 +90,40 @@ def test_every_finite_bf16_pattern(options, name, fused):
         ofy, ofa = oracle.fake_quantize(xh, rpg, rule)
         assert np.array_equal(fa.cpu().numpy().view(np.uint32), ofa.view(np.uint32)), what
         assert np.array_equal(_u16(fy), ofy), what
+
+
+@pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
+@pytest.mark.parametrize("rows_per_page", [1, 6])
+def test_every_finite_bf16_pattern_paged(options, rows_per_page, fused):
+    """The patterns in order as logical blocks of a paged cache, written into pages in a
+    seeded random order (every page its own scale group, from subnormal-amax pages up), then
+    gathered back to dense bf16 and float32."""
+    kv = options
+    kv.kvfp4_set_option("append_fused", fused)
+    xh = ARR["in_order/1"][0]
+    n_blocks = xh.shape[0] // rows_per_page
+    xh = xh[: n_blocks * rows_per_page]
+    n_pages = n_blocks + 3
+    table = np.random.default_rng(1).permutation(n_pages)[:n_blocks].astype(np.int32)
+    x = torch.from_numpy(xh.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    td = torch.from_numpy(table).to(DEV)
+    for rule in RULES:
+        codes = torch.zeros((n_pages, rows_per_page, D // 2), dtype=torch.uint8, device=DEV)
+        scales = torch.zeros((n_pages, rows_per_page, D // 16), dtype=torch.uint8, device=DEV)
+        amax = torch.zeros((n_pages,), dtype=torch.float32, device=DEV)
+        kv.kvfp4_quantize_paged(x, td, rows_per_page, codes, scales, amax, rule)
+        y = kv.kvfp4_dequantize_paged(codes, scales, amax, td, rows_per_page)
+        y32 = kv.kvfp4_dequantize_paged_f32(codes, scales, amax, td, rows_per_page)
+        torch.cuda.synchronize()
+        oc, os_, oa = oracle.quantize_paged(xh, table, rows_per_page, n_pages, rule)
+        what = (rows_per_page, fused, rule)
+        assert np.array_equal(amax.cpu().numpy().view(np.uint32), oa.view(np.uint32)), what
+        assert np.array_equal(scales.cpu().numpy(), os_), what
+        assert np.array_equal(codes.cpu().numpy(), oc), what
+        ref = oracle.dequantize_paged(oc, os_, oa, table, rows_per_page)
+        assert np.array_equal(_u16(y), ref), what
+        ref32 = oracle.dequantize_paged_f32(oc, os_, oa, table, rows_per_page)
+        assert np.array_equal(y32.cpu().numpy().view(np.uint32), ref32.view(np.uint32)), what
 
 
 @pytest.mark.parametrize("bits", [4, 2])
