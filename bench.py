@@ -237,7 +237,7 @@ def bench_rtn(device, steps=20, warmup=3):
     return res
 
 
-# ---- CPU baseline (oracle, single thread) -----------------------------------------------
+# ---- CPU baseline (the oracle on the host's threads and on one) -------------------------
 
 def _host_threads():
     """Worker threads for the parallel oracle runs: the host's cores, at most 16 (the CPU
