@@ -13,7 +13,8 @@ subnormal range to near the bf16 maximum):
     where the group's s_enc is a power of two);
   - rare outliers 2^8 .. 2^16 times larger (blocks that saturate the 4-max candidate).
 Checked in both quantize forms: codes, scale bytes, group amax, dequantize (bf16 and float32)
-of the GPU's own packed output, fake quantization.
+of the GPU's own packed output, fake quantization; every third case also through RTN INT4
+and INT2.
 """
 import numpy as np
 import pytest
@@ -111,3 +112,21 @@ def test_fuzz_matches_oracle(options, seed):
         assert np.array_equal(y32.cpu().numpy().view(np.uint32), oy32.view(np.uint32)), what
         assert np.array_equal(fa.cpu().numpy().view(np.uint32), ofa.view(np.uint32)), what
         assert np.array_equal(_u16(fy), ofy), what
+
+
+@pytest.mark.parametrize("seed", range(0, 60, 3))
+@pytest.mark.parametrize("bits", [4, 2])
+def test_fuzz_rtn_matches_oracle(seed, bits):
+    """The same blocks through RTN INT4/INT2 (per-block bf16 scale, round half to even):
+    codes, scales and the dequantization."""
+    import kv_cache_fp4_amd as kv
+    xh, _, _ = _case(seed)
+    x = torch.from_numpy(xh.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    c, s = kv.kvfp4_rtn_quantize(x, bits)
+    y = kv.kvfp4_rtn_dequantize(c, s, bits)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.rtn_quantize(xh, bits)
+    what = (seed, xh.shape, bits)
+    assert np.array_equal(_u16(s), os_), what
+    assert np.array_equal(c.cpu().numpy(), oc), what
+    assert np.array_equal(_u16(y), oracle.rtn_dequantize(oc, os_, bits)), what
