@@ -65,6 +65,61 @@ def test_attend_matches_oracle(tq, tk, H, D, tpg, q_scale):
     assert mx <= 2e-2 and rel <= 1e-2, (mx, rel, ref_max)
 
 
+def _attend_vs_oracle(q, k, v, tpg, rule="static_6"):
+    """Quantize k and v (bf16 [T, H, D]) on the GPU, attend, and compare with the oracle's
+    double attention over its own dequantized cache; returns (max |err|, rel RMS, max |ref|)."""
+    import kv_cache_fp4_amd as kv
+    tq, H, D = q.shape
+    tk = k.shape[0]
+    rpg = tpg * H
+    kc, ks, ka = kv.kvfp4_quantize(k.to(DEV), rpg, rule)
+    vc, vs, va = kv.kvfp4_quantize(v.to(DEV), rpg, rule)
+    o = kv.kvfp4_attend(q.to(DEV), kc, ks, ka, vc, vs, va, tpg, D ** -0.5)
+    torch.cuda.synchronize()
+    def deq(t):
+        return oracle.dequantize(*oracle.quantize(_u16(t).reshape(-1, D), rpg, rule),
+                                 rpg).reshape(tk, H, D)
+    kd, vd = deq(k), deq(v)
+    rows = np.arange(tq * H, dtype=np.int64)
+    ref = _f(oracle.attend_rows(_u16(q), kd, vd, D ** -0.5, rows)).astype(np.float64)
+    got = _f(_u16(o).reshape(-1, D)).astype(np.float64)
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    return err.max(), rel, np.abs(ref).max()
+
+
+def test_zero_keys_average_the_values():
+    """K = 0: every score is 0, so O is the plain mean of the dequantized V rows."""
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn((96, 2, 128), generator=g).to(torch.bfloat16)
+    k = torch.zeros((300, 2, 128), dtype=torch.bfloat16)
+    v = torch.randn((300, 2, 128), generator=g).to(torch.bfloat16)
+    mx, rel, _ = _attend_vs_oracle(q, k, v, 100)
+    assert mx <= 2e-2 and rel <= 1e-2, (mx, rel)
+
+
+def test_peaky_logits():
+    """Query scale 30 (logit standard deviation about 30): one key dominates each row, and
+    the running max moves on many steps."""
+    g = torch.Generator().manual_seed(8)
+    q = (torch.randn((130, 2, 128), generator=g) * 30.0).to(torch.bfloat16)
+    k = torch.randn((700, 2, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((700, 2, 128), generator=g).to(torch.bfloat16)
+    mx, rel, _ = _attend_vs_oracle(q, k, v, 350, "mse")
+    assert mx <= 2e-2 and rel <= 1e-2, (mx, rel)
+
+
+def test_tiny_values():
+    """V with group amax around 2^-100 (outputs near 2^-100: the relative criterion is the
+    one that bites) and K with amax around 2^-60 (all scores near 0)."""
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn((64, 3, 64), generator=g).to(torch.bfloat16)
+    k = (torch.randn((200, 3, 64), generator=g) * 2.0 ** -60).to(torch.bfloat16)
+    v = (torch.randn((200, 3, 64), generator=g) * 2.0 ** -100).to(torch.bfloat16)
+    mx, rel, ref_max = _attend_vs_oracle(q, k, v, 64)
+    assert ref_max > 0 and mx <= 2e-2 * ref_max and rel <= 1e-2, (mx, rel, ref_max)
+
+
 def test_single_key_returns_its_value_row():
     import kv_cache_fp4_amd as kv
     g = torch.Generator().manual_seed(3)
