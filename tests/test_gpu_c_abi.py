@@ -1,8 +1,10 @@
 """The library used from plain C: tests/c_abi/abi_roundtrip.c (built by __graft_entry__.build())
-allocates device buffers with hipMalloc, runs quantize + dequantize on a stream of its own
-for every rule, three group layouts and both quantize forms, compares every output byte with
-the oracle, and checks host-side argument errors.  It runs as its own process (its own HIP
-runtime)."""
+allocates device buffers with hipMalloc and, on a stream of its own, runs quantize +
+dequantize for every rule, three group layouts and both quantize forms, a paged quantize and
+gather through a shuffled block table (two rules), RTN INT4 and INT2 round trips, comparing
+every output byte with the oracle, and an attention call against the oracle's double
+attention (max |err| <= 2e-2, rel RMS <= 1e-2); it also checks host-side argument errors.
+It runs as its own process (its own HIP runtime)."""
 import os
 import subprocess
 
@@ -19,4 +21,6 @@ def test_c_program_round_trip_matches_oracle():
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith("OK")
-    assert r.stdout.count("bit-exact") == 18  # 3 layouts x 3 rules x 2 quantize forms
+    # 3 layouts x 3 rules x 2 quantize forms, 2 paged rules, 2 RTN widths
+    assert r.stdout.count("bit-exact") == 22
+    assert r.stdout.count("within tolerance") == 1
