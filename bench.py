@@ -98,13 +98,13 @@ class CacheWorkload:
         g0, g1 = c * self.cfg.groups_per_chunk, (c + 1) * self.cfg.groups_per_chunk
         return self.codes[r0:r1], self.scales[r0:r1], self.amax[g0:g1]
 
-    def quantize_chunk(self, c, src):
+    def quantize_chunk(self, c, src, opts=None):
         import kv_cache_fp4_amd as kv
         codes, scales, amax = self.slab(c)
-        kv.kvfp4_quantize(src, self.rpg, self.rule, codes, scales, amax)
+        kv.kvfp4_quantize(src, self.rpg, self.rule, codes, scales, amax, opts=opts)
 
-    def append(self):
-        self.quantize_chunk(self.cfg.chunks - 1, self.append_src)
+    def append(self, opts=None):
+        self.quantize_chunk(self.cfg.chunks - 1, self.append_src, opts)
 
     def dequantize_all(self):
         self.kv.kvfp4_dequantize(self.codes, self.scales, self.amax, self.rpg, y=self.out)
@@ -181,16 +181,12 @@ def bench_paged(device, steps=20, warmup=3):
            "ms_per_call": round(ms, 4), "bytes_per_call": w.dequant_bytes(),
            "GBps": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     # Quantizing every block into its page (same bytes), in both quantize forms.
-    quant = lambda: w.kv.kvfp4_quantize_paged(w.src, w.table, w.rpp, w.codes, w.scales,  # noqa: E731
-                                              w.amax, "static_6")
-    fused_before = w.kv.kvfp4_get_option("append_fused")
-    try:
-        for fused, key in ((1, "quantize"), (0, "quantize_three_kernel")):
-            w.kv.kvfp4_set_option("append_fused", fused)
-            qms = _time_calls(quant, device, max(steps // 2, 3), 2)
-            res[key] = {"ms": round(qms, 4), "GBps": round(w.dequant_bytes() / (qms * 1e-3) / 1e9, 2)}
-    finally:
-        w.kv.kvfp4_set_option("append_fused", fused_before)
+    for form, key in (("auto", "quantize"), ("three_kernel", "quantize_three_kernel")):
+        opts = w.kv.quantize_opts(form)
+        quant = lambda: w.kv.kvfp4_quantize_paged(w.src, w.table, w.rpp, w.codes, w.scales,  # noqa: E731
+                                                  w.amax, "static_6", opts=opts)
+        qms = _time_calls(quant, device, max(steps // 2, 3), 2)
+        res[key] = {"ms": round(qms, 4), "GBps": round(w.dequant_bytes() / (qms * 1e-3) / 1e9, 2)}
     del w
     torch.cuda.empty_cache()
     return res
@@ -524,12 +520,8 @@ def main(argv=None):
 
     # The append again in the three-kernel form (clear, group amax, encode) for comparison
     # with the one-kernel form the step used.
-    fused_before = w.kv.kvfp4_get_option("append_fused")
-    w.kv.kvfp4_set_option("append_fused", 0)
-    try:
-        ms_ap3 = _time_calls(w.append, dev, max(args.steps, 3), 2)
-    finally:
-        w.kv.kvfp4_set_option("append_fused", fused_before)
+    three = w.kv.quantize_opts("three_kernel")
+    ms_ap3 = _time_calls(lambda: w.append(three), dev, max(args.steps, 3), 2)
 
     step_bytes = w.append_bytes() + w.dequant_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
@@ -567,7 +559,7 @@ def main(argv=None):
                      "bytes_per_launch": w.dequant_bytes(), "ms_per_launch": round(ms_dq, 4)},
         "breakdown": {"append_ms": round(ms_ap, 4), "append_GBps": round(ap_gbs, 2),
                       "append_bytes": w.append_bytes(),
-                      "append_form": "one-kernel" if fused_before else "three-kernel",
+                      "append_form": "one-kernel",
                       "append_three_kernel_ms": round(ms_ap3, 4),
                       "dequant_ms": round(ms_dq, 4), "dequant_GBps": round(dq_gbs, 2)},
         "per_layer_dequant": {"launches": n_launch, "ms_total": round(ms_pl, 4),

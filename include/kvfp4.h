@@ -32,9 +32,9 @@
  *
  * Conventions for every entry point:
  *   - pointers are DEVICE pointers unless stated; the caller allocates and frees all of
- *     them; the library never allocates, never synchronizes, keeps no state besides a
- *     thread-local copy of the last HIP error and the two process-wide options of
- *     kvfp4_set_option, and is reentrant across streams;
+ *     them; the library never allocates, never synchronizes, keeps no mutable state besides
+ *     a thread-local copy of the last HIP error (everything a call needs arrives with the
+ *     call), and is reentrant across streams and threads;
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work is only
  *     enqueued, the call returns before it runs;
  *   - argument errors are detected on the host and returned before anything is enqueued;
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KVFP4_ABI_VERSION 1
+#define KVFP4_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum kvfp4_status {
@@ -93,7 +93,8 @@ enum kvfp4_rule {
  * included) has at least 528 elements, a hand-off clear, one kernel that computes the group
  * amax and encodes (it borrows three dwords of each group's codes for the hand-off; the
  * codes are complete when the call's work ends), and a finish kernel; otherwise amax
- * clear, group amax, encode.  Both give the same bytes.
+ * clear, group amax, encode.  Both give the same bytes.  (These are the default options of
+ * kvfp4_quantize_ex, below.)
  */
 int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
                    int32_t rule, uint8_t* codes, uint8_t* scales, float* group_amax,
@@ -241,25 +242,43 @@ int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
                        int64_t* codes_bytes, int64_t* scales_bytes, int64_t* n_groups);
 
 /*
- * Process-wide options, read when a call enqueues its work (work already enqueued or
- * captured in a graph keeps the values it was enqueued with).  Neither changes any output.
- *   KVFP4_OPT_APPEND_FUSED    1 (default): kvfp4_quantize, kvfp4_quantize_paged and
- *                             kvfp4_fake_quantize (not in place) take the one-kernel
- *                             amax + encode form where it applies; 0: always the
- *                             three-kernel form.
- *   KVFP4_OPT_APPEND_WAIT_US  in the one-kernel form, the longest time (microseconds) an
- *                             encode workgroup waits for its group amax before computing it
- *                             itself from the input; 0 = never wait; default 20000, at
- *                             most 60000000.
- * kvfp4_set_option returns KVFP4_EINVAL for an unknown option or a value out of range;
- * kvfp4_get_option writes the current value to *value (host pointer).
+ * Per-call quantize options: how kvfp4_quantize_ex, kvfp4_quantize_paged_ex and
+ * kvfp4_fake_quantize_ex enqueue their work.  They never change an output byte.  [P-KV]
+ * "Programmatic Configuration" carries its settings in a configuration object handed to the
+ * call that uses them; these options travel the same way (no process-wide settings).
+ *   form     KVFP4_FORM_AUTO (the default): one kernel computes the group amax and encodes
+ *            wherever that applies (not in place, every group -- the last one included --
+ *            at least 528 elements, 32-bit grid); otherwise three kernels (clear the amax
+ *            words, group amax, encode).  KVFP4_FORM_THREE_KERNEL: always three kernels.
+ *   wait_us  in the one-kernel form, the longest time in microseconds an encode workgroup
+ *            waits for its group amax before it computes the amax itself from the input
+ *            (the same value); 0 = never wait; default 20000; at most 60000000.
+ * opts == NULL means the defaults, which is what the calls without the _ex suffix use.  An
+ * unknown form or a wait_us out of range returns KVFP4_EINVAL before anything is enqueued.
+ * The struct is read during the call only (host memory, owned by the caller).
  */
-enum kvfp4_option {
-  KVFP4_OPT_APPEND_FUSED = 1,
-  KVFP4_OPT_APPEND_WAIT_US = 2
+enum kvfp4_form {
+  KVFP4_FORM_AUTO = 0,
+  KVFP4_FORM_THREE_KERNEL = 1
 };
-int kvfp4_set_option(int32_t option, int64_t value);
-int kvfp4_get_option(int32_t option, int64_t* value);
+struct kvfp4_quantize_opts {
+  int32_t form;     /* enum kvfp4_form */
+  int64_t wait_us;  /* 0 .. 60000000 */
+};
+#define KVFP4_QUANTIZE_OPTS_DEFAULT {KVFP4_FORM_AUTO, 20000}
+
+/* kvfp4_quantize, kvfp4_quantize_paged and kvfp4_fake_quantize with explicit options (same
+ * arguments otherwise, same results). */
+int kvfp4_quantize_ex(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
+                      int32_t rule, uint8_t* codes, uint8_t* scales, float* group_amax,
+                      const struct kvfp4_quantize_opts* opts, void* stream);
+int kvfp4_quantize_paged_ex(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page,
+                            int32_t head_dim, int32_t rule, const int32_t* block_table,
+                            int64_t n_pages, uint8_t* codes, uint8_t* scales, float* page_amax,
+                            const struct kvfp4_quantize_opts* opts, void* stream);
+int kvfp4_fake_quantize_ex(const uint16_t* x, int64_t rows, int32_t head_dim,
+                           int64_t rows_per_group, int32_t rule, float* group_amax, uint16_t* y,
+                           const struct kvfp4_quantize_opts* opts, void* stream);
 
 /* Diagnostics. */
 const char* kvfp4_status_str(int status); /* static string, never NULL */

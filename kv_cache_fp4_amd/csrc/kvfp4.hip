@@ -33,8 +33,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "kvfp4.h"
 #include "kvfp4_device.hpp"
 
@@ -810,24 +808,25 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
   return launched();
 }
 
-// Process-wide options (kvfp4_set_option).
-std::atomic<int64_t> g_opt_append_fused{1};
-std::atomic<int64_t> g_opt_append_wait_us{20000};
-
-// Wall-clock ticks in `us` microseconds on the current device (its wall-clock rate is read
-// once per device; 100 MHz if the runtime does not report it).
+// Wall-clock ticks in `us` microseconds on the current device (100 MHz if the runtime does
+// not report the device's wall-clock rate).
 uint64_t wall_ticks(int64_t us) {
-  static std::atomic<int> khz_of[64];
   int dev = 0, khz = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  if (dev >= 0 && dev < 64) khz = khz_of[dev].load(std::memory_order_relaxed);
-  if (khz <= 0) {
-    if (dev < 0 || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
-        khz <= 0)
-      khz = 100000;
-    if (dev >= 0 && dev < 64) khz_of[dev].store(khz, std::memory_order_relaxed);
-  }
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    khz = 100000;
   return (uint64_t)us * (uint64_t)khz / 1000u;
+}
+
+// Per-call quantize options, checked and defaulted (NULL = KVFP4_QUANTIZE_OPTS_DEFAULT).
+constexpr int64_t kMaxWaitUs = INT64_C(60000000);
+
+int read_opts(const kvfp4_quantize_opts* in, kvfp4_quantize_opts* out) {
+  const kvfp4_quantize_opts def = KVFP4_QUANTIZE_OPTS_DEFAULT;
+  *out = in ? *in : def;
+  if (out->form != KVFP4_FORM_AUTO && out->form != KVFP4_FORM_THREE_KERNEL) return KVFP4_EINVAL;
+  if (out->wait_us < 0 || out->wait_us > kMaxWaitUs) return KVFP4_EINVAL;
+  return KVFP4_OK;
 }
 
 // One-launch append (three launches: hand-off clear, append, finish) when it applies: not in
@@ -836,7 +835,8 @@ uint64_t wall_ticks(int64_t us) {
 template <int RULE, int THREADS>
 int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
-                  float* group_amax, uint16_t* fake_y, hipStream_t s, bool* used) {
+                  float* group_amax, uint16_t* fake_y, int64_t wait_us, hipStream_t s,
+                  bool* used) {
   *used = false;
   const int64_t upr = head_dim / 8;
   const int64_t upg = (rpg < rows ? rpg : rows) * upr;
@@ -848,7 +848,6 @@ int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
   if (ng * (ta + te) > INT32_MAX) return KVFP4_OK;
   int64_t lag = (kAppendLagUnits + upg - 1) / upg;
   if (lag > ng) lag = ng;
-  const int64_t wait_us = g_opt_append_wait_us.load(std::memory_order_relaxed);
   Append f;
   f.units_total = total;
   f.units_per_group = upg;
@@ -887,29 +886,32 @@ int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
   return launched();
 }
 
-// Shared body of the dense, paged and fake quantize entry points (arguments already
-// checked).  With fake_y set, the encode pass writes bf16 there instead of codes/scales.
-// Not-in-place calls take the one-launch append where it applies (and the option allows);
-// the rest take three kernels: clear, group amax, encode.
+// Shared body of the dense, paged and fake quantize entry points (arguments and options
+// already checked).  With fake_y set, the encode pass writes bf16 there instead of
+// codes/scales.  Not-in-place calls take the one-launch append where it applies (and the
+// options allow); the rest take three kernels: clear, group amax, encode.
 int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
-                  float* group_amax, uint16_t* fake_y, hipStream_t s) {
-  if ((const void*)fake_y != (const void*)x &&
-      g_opt_append_fused.load(std::memory_order_relaxed) != 0) {
+                  float* group_amax, uint16_t* fake_y, const kvfp4_quantize_opts& o,
+                  hipStream_t s) {
+  if ((const void*)fake_y != (const void*)x && o.form == KVFP4_FORM_AUTO) {
     bool used = false;
     int arc;
     switch (rule) {
       case KVFP4_RULE_STATIC6:
         arc = launch_append<KVFP4_RULE_STATIC6, kAppendStaticThreads>(
-            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, o.wait_us, s,
+            &used);
         break;
       case KVFP4_RULE_STATIC4:
         arc = launch_append<KVFP4_RULE_STATIC4, kAppendStaticThreads>(
-            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, o.wait_us, s,
+            &used);
         break;
       default:
         arc = launch_append<KVFP4_RULE_MSE, kAppendMseThreads>(
-            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, s, &used);
+            x, rows, head_dim, rpg, table, n_pages, codes, scales, group_amax, fake_y, o.wait_us, s,
+            &used);
         break;
     }
     if (used) return arc;
@@ -980,20 +982,34 @@ int set_last_hip_error(int e) {
 
 using namespace kvfp4;
 
-extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
-                              int64_t rows_per_group, int32_t rule, uint8_t* codes,
-                              uint8_t* scales, float* group_amax, void* stream) {
-  if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
-    return KVFP4_EINVAL;
+static bool known_rule(int32_t rule) {
+  return rule == KVFP4_RULE_STATIC6 || rule == KVFP4_RULE_STATIC4 || rule == KVFP4_RULE_MSE;
+}
+
+extern "C" int kvfp4_quantize_ex(const uint16_t* x, int64_t rows, int32_t head_dim,
+                                 int64_t rows_per_group, int32_t rule, uint8_t* codes,
+                                 uint8_t* scales, float* group_amax,
+                                 const kvfp4_quantize_opts* opts, void* stream) {
+  if (!known_rule(rule)) return KVFP4_EINVAL;
+  kvfp4_quantize_opts o;
+  int rc = read_opts(opts, &o);
+  if (rc != KVFP4_OK) return rc;
   int64_t ng = 0;
-  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
+  rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!x || !codes || !scales || !group_amax) return KVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(group_amax, 4))
     return KVFP4_EALIGN;
   return quantize_impl(x, rows, head_dim, rows_per_group, rule, nullptr, 0, codes, scales,
-                       group_amax, nullptr, (hipStream_t)stream);
+                       group_amax, nullptr, o, (hipStream_t)stream);
+}
+
+extern "C" int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
+                              int64_t rows_per_group, int32_t rule, uint8_t* codes,
+                              uint8_t* scales, float* group_amax, void* stream) {
+  return kvfp4_quantize_ex(x, rows, head_dim, rows_per_group, rule, codes, scales, group_amax,
+                           nullptr, stream);
 }
 
 static int dequantize_entry(const uint8_t* codes, const uint8_t* scales, const float* group_amax,
@@ -1026,19 +1042,29 @@ extern "C" int kvfp4_dequantize_f32(const uint8_t* codes, const uint8_t* scales,
                           stream);
 }
 
-extern "C" int kvfp4_fake_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
-                                   int64_t rows_per_group, int32_t rule, float* group_amax,
-                                   uint16_t* y, void* stream) {
-  if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
-    return KVFP4_EINVAL;
+extern "C" int kvfp4_fake_quantize_ex(const uint16_t* x, int64_t rows, int32_t head_dim,
+                                      int64_t rows_per_group, int32_t rule, float* group_amax,
+                                      uint16_t* y, const kvfp4_quantize_opts* opts,
+                                      void* stream) {
+  if (!known_rule(rule)) return KVFP4_EINVAL;
+  kvfp4_quantize_opts o;
+  int rc = read_opts(opts, &o);
+  if (rc != KVFP4_OK) return rc;
   int64_t ng = 0;
-  int rc = check_shape(rows, head_dim, rows_per_group, &ng);
+  rc = check_shape(rows, head_dim, rows_per_group, &ng);
   if (rc != KVFP4_OK) return rc;
   if (rows == 0) return KVFP4_OK;
   if (!x || !group_amax || !y) return KVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(group_amax, 4)) return KVFP4_EALIGN;
   return quantize_impl(x, rows, head_dim, rows_per_group, rule, nullptr, 0, nullptr, nullptr,
-                       group_amax, y, (hipStream_t)stream);
+                       group_amax, y, o, (hipStream_t)stream);
+}
+
+extern "C" int kvfp4_fake_quantize(const uint16_t* x, int64_t rows, int32_t head_dim,
+                                   int64_t rows_per_group, int32_t rule, float* group_amax,
+                                   uint16_t* y, void* stream) {
+  return kvfp4_fake_quantize_ex(x, rows, head_dim, rows_per_group, rule, group_amax, y, nullptr,
+                                stream);
 }
 
 // Paged cache: shared checks of the two paged entry points.
@@ -1056,20 +1082,31 @@ static int check_paged(int64_t n_blocks, int64_t rows_per_page, int32_t head_dim
   return KVFP4_OK;
 }
 
-extern "C" int kvfp4_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page,
-                                    int32_t head_dim, int32_t rule, const int32_t* block_table,
-                                    int64_t n_pages, uint8_t* codes, uint8_t* scales,
-                                    float* page_amax, void* stream) {
-  if (rule != KVFP4_RULE_STATIC6 && rule != KVFP4_RULE_STATIC4 && rule != KVFP4_RULE_MSE)
-    return KVFP4_EINVAL;
-  int rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
+extern "C" int kvfp4_quantize_paged_ex(const uint16_t* x, int64_t n_blocks,
+                                       int64_t rows_per_page, int32_t head_dim, int32_t rule,
+                                       const int32_t* block_table, int64_t n_pages,
+                                       uint8_t* codes, uint8_t* scales, float* page_amax,
+                                       const kvfp4_quantize_opts* opts, void* stream) {
+  if (!known_rule(rule)) return KVFP4_EINVAL;
+  kvfp4_quantize_opts o;
+  int rc = read_opts(opts, &o);
+  if (rc != KVFP4_OK) return rc;
+  rc = check_paged(n_blocks, rows_per_page, head_dim, n_pages, block_table);
   if (rc != KVFP4_OK) return rc;
   if (n_blocks == 0) return KVFP4_OK;
   if (!x || !codes || !scales || !page_amax) return KVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(page_amax, 4))
     return KVFP4_EALIGN;
   return quantize_impl(x, n_blocks * rows_per_page, head_dim, rows_per_page, rule, block_table,
-                       n_pages, codes, scales, page_amax, nullptr, (hipStream_t)stream);
+                       n_pages, codes, scales, page_amax, nullptr, o, (hipStream_t)stream);
+}
+
+extern "C" int kvfp4_quantize_paged(const uint16_t* x, int64_t n_blocks, int64_t rows_per_page,
+                                    int32_t head_dim, int32_t rule, const int32_t* block_table,
+                                    int64_t n_pages, uint8_t* codes, uint8_t* scales,
+                                    float* page_amax, void* stream) {
+  return kvfp4_quantize_paged_ex(x, n_blocks, rows_per_page, head_dim, rule, block_table, n_pages,
+                                 codes, scales, page_amax, nullptr, stream);
 }
 
 static int dequantize_paged_entry(const uint8_t* codes, const uint8_t* scales,
@@ -1175,34 +1212,5 @@ extern "C" const char* kvfp4_status_str(int status) {
 }
 
 extern "C" int kvfp4_abi_version(void) { return KVFP4_ABI_VERSION; }
-
-extern "C" int kvfp4_set_option(int32_t option, int64_t value) {
-  switch (option) {
-    case KVFP4_OPT_APPEND_FUSED:
-      if (value != 0 && value != 1) return KVFP4_EINVAL;
-      g_opt_append_fused.store(value, std::memory_order_relaxed);
-      return KVFP4_OK;
-    case KVFP4_OPT_APPEND_WAIT_US:
-      if (value < 0 || value > INT64_C(60000000)) return KVFP4_EINVAL;
-      g_opt_append_wait_us.store(value, std::memory_order_relaxed);
-      return KVFP4_OK;
-    default:
-      return KVFP4_EINVAL;
-  }
-}
-
-extern "C" int kvfp4_get_option(int32_t option, int64_t* value) {
-  if (!value) return KVFP4_EINVAL;
-  switch (option) {
-    case KVFP4_OPT_APPEND_FUSED:
-      *value = g_opt_append_fused.load(std::memory_order_relaxed);
-      return KVFP4_OK;
-    case KVFP4_OPT_APPEND_WAIT_US:
-      *value = g_opt_append_wait_us.load(std::memory_order_relaxed);
-      return KVFP4_OK;
-    default:
-      return KVFP4_EINVAL;
-  }
-}
 
 extern "C" int kvfp4_last_hip_error(void) { return g_last_hip_error; }

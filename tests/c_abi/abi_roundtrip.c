@@ -1,8 +1,8 @@
 /*
  * abi_roundtrip.c -- a plain C program that uses libkvfp4 through its C ABI alone:
  * hipMalloc'd device buffers, a HIP stream of its own, every scale rule, several group
- * layouts, both quantize forms (KVFP4_OPT_APPEND_FUSED), and host-side argument errors.  Its outputs are compared byte for byte with the
- * oracle (test infrastructure, loaded as its own library).  Exit status 0 = all equal.
+ * layouts, both quantize forms (per-call options of kvfp4_quantize_ex), and host-side
+ * argument errors.  Its outputs are compared byte for byte with the oracle (test infrastructure, loaded as its own library).  Exit status 0 = all equal.
  *
  * Input: bf16 bit patterns drawn from a fixed-seed xorshift generator with the exponent
  * limited to [2^-17, 2^13) (finite, every group amax inside the contract), plus an
@@ -69,7 +69,8 @@ static double bf16_value(uint16_t h) {
   return (double)f;
 }
 
-static int run_case(int64_t rows, int d, int64_t rpg, int rule, hipStream_t st) {
+static int run_case(int64_t rows, int d, int64_t rpg, int rule,
+                    const struct kvfp4_quantize_opts* opts, hipStream_t st) {
   const int64_t n = rows * d, ng = (rows + rpg - 1) / rpg;
   uint16_t* x = (uint16_t*)malloc(n * 2);
   fill_bf16(x, n, 110, 30);  /* magnitudes 2^-17 .. 2^13 */
@@ -91,8 +92,8 @@ static int run_case(int64_t rows, int d, int64_t rpg, int rule, hipStream_t st) 
   CHECK_HIP(hipMalloc(&da, ng * 4));
   CHECK_HIP(hipMalloc(&dy, n * 2));
   CHECK_HIP(hipMemcpyAsync(dx, x, n * 2, hipMemcpyHostToDevice, st));
-  int rc = kvfp4_quantize((const uint16_t*)dx, rows, d, rpg, rule, (uint8_t*)dc, (uint8_t*)ds,
-                          (float*)da, st);
+  int rc = kvfp4_quantize_ex((const uint16_t*)dx, rows, d, rpg, rule, (uint8_t*)dc,
+                             (uint8_t*)ds, (float*)da, opts, st);
   if (rc == KVFP4_OK)
     rc = kvfp4_dequantize((const uint8_t*)dc, (const uint8_t*)ds, (const float*)da, rows, d, rpg,
                           (uint16_t*)dy, st);
@@ -120,7 +121,7 @@ static int run_case(int64_t rows, int d, int64_t rpg, int rule, hipStream_t st) 
 
 /* Paged cache: 9 logical blocks of 5 rows into 12 pages in shuffled order, one entry out of
  * range (skipped); quantize into the pages, then gather back. */
-static int run_paged(int rule, hipStream_t st) {
+static int run_paged(int rule, const struct kvfp4_quantize_opts* opts, hipStream_t st) {
   enum { NB = 9, RPP = 5, D = 128, NP = 12 };
   const int32_t table[NB] = {7, 2, 11, 0, 5, -1, 9, 3, 1};
   const int64_t n = (int64_t)NB * RPP * D, pn = (int64_t)NP * RPP * D;
@@ -148,8 +149,8 @@ static int run_paged(int rule, hipStream_t st) {
   CHECK_HIP(hipMemsetAsync(dy, 0, n * 2, st));
   CHECK_HIP(hipMemcpyAsync(dx, x, n * 2, hipMemcpyHostToDevice, st));
   CHECK_HIP(hipMemcpyAsync(dt, table, sizeof table, hipMemcpyHostToDevice, st));
-  int rc = kvfp4_quantize_paged((const uint16_t*)dx, NB, RPP, D, rule, (const int32_t*)dt, NP,
-                                (uint8_t*)dc, (uint8_t*)ds, (float*)da, st);
+  int rc = kvfp4_quantize_paged_ex((const uint16_t*)dx, NB, RPP, D, rule, (const int32_t*)dt,
+                                   NP, (uint8_t*)dc, (uint8_t*)ds, (float*)da, opts, st);
   if (rc == KVFP4_OK)
     rc = kvfp4_dequantize_paged((const uint8_t*)dc, (const uint8_t*)ds, (const float*)da,
                                 (const int32_t*)dt, NB, RPP, D, NP, (uint16_t*)dy, st);
@@ -298,18 +299,20 @@ int main(void) {
   CHECK_HIP(hipStreamCreate(&st));
   int bad = 0;
   /* both quantize forms (the one-kernel form applies to the first and third layouts) */
-  for (int fused = 1; fused >= 0; --fused) {
-    if (kvfp4_set_option(KVFP4_OPT_APPEND_FUSED, fused) != KVFP4_OK) bad = 1;
-    printf("append form: %s\n", fused ? "one kernel where it applies" : "three kernels");
+  const struct kvfp4_quantize_opts forms[2] = {KVFP4_QUANTIZE_OPTS_DEFAULT,
+                                               {KVFP4_FORM_THREE_KERNEL, 20000}};
+  for (int f = 0; f < 2; ++f) {
+    printf("append form: %s\n", f == 0 ? "one kernel where it applies" : "three kernels");
     for (int rule = 0; rule < 3; ++rule) {
-      bad |= run_case(1000, 128, 300, rule, st);
-      bad |= run_case(37, 64, 10, rule, st);
-      bad |= run_case(513, 256, 513, rule, st);
+      bad |= run_case(1000, 128, 300, rule, &forms[f], st);
+      bad |= run_case(37, 64, 10, rule, &forms[f], st);
+      bad |= run_case(513, 256, 513, rule, &forms[f], st);
     }
   }
-  if (kvfp4_set_option(KVFP4_OPT_APPEND_FUSED, 1) != KVFP4_OK) bad = 1;
-  bad |= run_paged(0, st);
-  bad |= run_paged(2, st);
+  /* the plain entry point (NULL options) */
+  bad |= run_case(1000, 128, 300, KVFP4_RULE_MSE, NULL, st);
+  bad |= run_paged(0, NULL, st);
+  bad |= run_paged(2, &forms[1], st);
   bad |= run_rtn(4, st);
   bad |= run_rtn(2, st);
   bad |= run_attend(st);
@@ -320,13 +323,15 @@ int main(void) {
   int e1 = kvfp4_quantize((const uint16_t*)(b + 8), 4, 64, 4, 0, b + 4096, b + 8192, (float*)(b + 12288), st);
   int e2 = kvfp4_dequantize(b, b + 4096, (const float*)(b + 8192), 4, 96, 4, (uint16_t*)(b + 12288), st);
   int e3 = kvfp4_quantize((const uint16_t*)b, 4, 64, 4, 7, b + 4096, b + 8192, (float*)(b + 12288), st);
-  int64_t ov = -1;
-  int e4 = kvfp4_set_option(99, 0);
-  int e5 = kvfp4_get_option(KVFP4_OPT_APPEND_WAIT_US, &ov);
-  printf("errors: misaligned x -> %d, head_dim 96 -> %d, rule 7 -> %d, option 99 -> %d\n", e1,
-         e2, e3, e4);
+  const struct kvfp4_quantize_opts bad_form = {7, 20000}, bad_wait = {KVFP4_FORM_AUTO, -1};
+  int e4 = kvfp4_quantize_ex((const uint16_t*)b, 4, 64, 4, 0, b + 4096, b + 8192,
+                             (float*)(b + 12288), &bad_form, st);
+  int e5 = kvfp4_fake_quantize_ex((const uint16_t*)b, 4, 64, 4, 0, (float*)(b + 12288),
+                                  (uint16_t*)(b + 16384), &bad_wait, st);
+  printf("errors: misaligned x -> %d, head_dim 96 -> %d, rule 7 -> %d, form 7 -> %d, "
+         "wait -1 -> %d\n", e1, e2, e3, e4, e5);
   bad |= !(e1 == KVFP4_EALIGN && e2 == KVFP4_EUNSUPPORTED && e3 == KVFP4_EINVAL &&
-           e4 == KVFP4_EINVAL && e5 == KVFP4_OK && ov >= 0);
+           e4 == KVFP4_EINVAL && e5 == KVFP4_EINVAL);
   CHECK_HIP(hipFree(p));
   CHECK_HIP(hipStreamDestroy(st));
   printf("%s\n", bad ? "FAILED" : "OK");

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.kvfp4_abi_version() == 1
+    assert lib.kvfp4_abi_version() == 2
     for s in range(5):
         assert lib.kvfp4_status_str(s)
     assert b"unknown" in lib.kvfp4_status_str(99)
@@ -243,28 +243,62 @@ def test_f32_and_fake_zero_rows_are_noops():
     assert fq(rows=0, x=None, amax=None, y=None) == KVFP4_OK
 
 
-def test_options_set_get_and_reject():
-    """The two process-wide options: defaults, round trip, rejected values (host only)."""
-    import ctypes
+def qx(opts, **kw):
+    a = dict(x=A16, rows=64, d=128, rpg=64, rule=0, codes=A16, scales=A16, amax=A16)
+    a.update(kw)
+    return lib.kvfp4_quantize_ex(a["x"], a["rows"], a["d"], a["rpg"], a["rule"], a["codes"],
+                                 a["scales"], a["amax"], opts, None)
 
-    import kv_cache_fp4_amd as kv
-    L = kv.lib
-    v = ctypes.c_int64()
-    assert L.kvfp4_get_option(1, ctypes.byref(v)) == 0 and v.value in (0, 1)
-    saved_fused = v.value
-    assert L.kvfp4_get_option(2, ctypes.byref(v)) == 0 and v.value >= 0
-    saved_wait = v.value
-    try:
-        for opt, good, bad in ((1, (0, 1), (-1, 2, 7)), (2, (0, 1, 20000, 60000000), (-1, 60000001))):
-            for g in good:
-                assert L.kvfp4_set_option(opt, g) == 0
-                assert L.kvfp4_get_option(opt, ctypes.byref(v)) == 0 and v.value == g
-            for b in bad:
-                assert L.kvfp4_set_option(opt, b) == 1
-                assert L.kvfp4_get_option(opt, ctypes.byref(v)) == 0 and v.value == good[-1]
-        assert L.kvfp4_set_option(0, 1) == 1 and L.kvfp4_set_option(3, 1) == 1
-        assert L.kvfp4_get_option(3, ctypes.byref(v)) == 1
-        assert L.kvfp4_get_option(1, None) == 1
-    finally:
-        L.kvfp4_set_option(1, saved_fused)
-        L.kvfp4_set_option(2, saved_wait)
+
+@pytest.mark.parametrize("form,wait,want", [
+    (2, 20000, KVFP4_EINVAL), (-1, 20000, KVFP4_EINVAL), (0, -1, KVFP4_EINVAL),
+    (1, 60000001, KVFP4_EINVAL), (0, 1 << 40, KVFP4_EINVAL),
+])
+def test_quantize_options_rejected_per_call(form, wait, want):
+    """Bad per-call options are argument errors of that call, found before anything is
+    enqueued (the pointers here are fake: nothing may be launched), on every _ex entry."""
+    o = ctypes.byref(kv.QuantizeOpts(form, wait))
+    assert qx(o) == want
+    assert lib.kvfp4_quantize_paged_ex(A16, 4, 24, 128, 0, A16, 8, A16, A16, A16, o, None) == want
+    assert lib.kvfp4_fake_quantize_ex(A16, 64, 128, 64, 0, A16, A16, o, None) == want
+
+
+@pytest.mark.parametrize("form,wait", [(0, 0), (0, 20000), (1, 0), (1, 60000000)])
+def test_quantize_options_accepted(form, wait):
+    """Valid options with zero rows: accepted, nothing to do (no device needed)."""
+    o = ctypes.byref(kv.QuantizeOpts(form, wait))
+    assert qx(o, rows=0, x=None, codes=None, scales=None, amax=None) == KVFP4_OK
+    assert lib.kvfp4_quantize_paged_ex(None, 0, 24, 128, 0, None, 8, None, None, None, o,
+                                       None) == KVFP4_OK
+    assert lib.kvfp4_fake_quantize_ex(None, 0, 128, 64, 0, None, None, o, None) == KVFP4_OK
+    # NULL options are the defaults
+    assert qx(None, rows=0, x=None, codes=None, scales=None, amax=None) == KVFP4_OK
+
+
+def test_ex_entries_check_arguments_like_the_plain_ones():
+    o = ctypes.byref(kv.quantize_opts())
+    assert qx(o, rule=3) == KVFP4_EINVAL
+    assert qx(o, d=96) == KVFP4_EUNSUPPORTED
+    assert qx(o, x=A16 + 8) == KVFP4_EALIGN
+    assert qx(o, rpg=0) == KVFP4_EINVAL
+
+
+def test_library_keeps_no_mutable_global_state():
+    """The only writable object the library defines in its own namespace is the thread-local
+    last HIP error; every other kvfp4:: object is a kernel's host-side launch handle (a
+    function signature).  Read from the ELF symbol table of the built library."""
+    import subprocess
+    out = subprocess.run(["readelf", "-sW", kv.LIB_PATH], check=True, capture_output=True,
+                         text=True).stdout
+    dem = subprocess.run(["c++filt"], input=out, check=True, capture_output=True, text=True).stdout
+    objs = []
+    for line in dem.splitlines():
+        f = line.split(None, 7)
+        if len(f) == 8 and f[3] in ("OBJECT", "TLS") and f[6] != "UND" and "kvfp4" in f[7]:
+            objs.append((f[3], f[7]))
+    tls = [n for t, n in objs if t == "TLS"]
+    assert tls == ["kvfp4::(anonymous namespace)::g_last_hip_error"], tls
+    others = [n for t, n in objs if t == "OBJECT"]
+    assert others, "expected the kernels' launch handles"
+    for n in others:
+        assert "_kernel" in n and "(" in n, n

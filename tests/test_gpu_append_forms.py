@@ -61,20 +61,20 @@ def _one_kernel_applies(rows, d, rpg):
 
 
 @pytest.fixture
-def options():
-    import kv_cache_fp4_amd as kv
-    saved = {k: kv.kvfp4_get_option(k) for k in kv.OPTIONS}
-    yield kv
-    for k, v in saved.items():
-        kv.kvfp4_set_option(k, v)
+def kv():
+    import kv_cache_fp4_amd
+    return kv_cache_fp4_amd
+
+
+def _form_opts(kv, form):
+    return kv.quantize_opts("three_kernel" if form == "three_kernels" else "auto",
+                            0 if form == "one_kernel_no_wait" else 20000)
 
 
 @pytest.mark.parametrize("form", ["one_kernel", "three_kernels", "one_kernel_no_wait"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{d}/{g}" for r, d, g in SHAPES])
-def test_quantize_forms_match_oracle(options, shape, form):
-    kv = options
-    kv.kvfp4_set_option("append_fused", 0 if form == "three_kernels" else 1)
-    kv.kvfp4_set_option("append_wait_us", 0 if form == "one_kernel_no_wait" else 20000)
+def test_quantize_forms_match_oracle(kv, shape, form):
+    opts = _form_opts(kv, form)
     rows, d, rpg = shape
     x = _x(rows, d, rows + d)
     xh = _u16(x)
@@ -84,10 +84,11 @@ def test_quantize_forms_match_oracle(options, shape, form):
         cb, codes = _guarded(rows * d // 2, torch.uint8, 0xA5)
         sb, scales = _guarded(rows * d // 16, torch.uint8, 0x5A)
         ab, amax = _guarded(ng, torch.float32, -7.0)
-        kv.kvfp4_quantize(xd, rpg, rule, codes, scales, amax)
+        kv.kvfp4_quantize(xd, rpg, rule, codes, scales, amax, opts=opts)
         fb, fy = _guarded(rows * d, torch.int16, 0x3C3C)
         fab, famax = _guarded(ng, torch.float32, -7.0)
-        kv.kvfp4_fake_quantize(xd, rpg, rule, y=fy.view(rows, d), group_amax=famax)
+        kv.kvfp4_fake_quantize(xd, rpg, rule, y=fy.view(rows, d).view(torch.bfloat16),
+                               group_amax=famax, opts=opts)
         torch.cuda.synchronize()
         oc, os_, oa = oracle.quantize(xh, rpg, rule)
         ofy, ofa = oracle.fake_quantize(xh, rpg, rule)
@@ -101,8 +102,7 @@ def test_quantize_forms_match_oracle(options, shape, form):
         assert np.array_equal(_u16(fy).reshape(ofy.shape), ofy), what
 
 
-def test_fake_quantize_in_place_matches_oracle(options):
-    kv = options
+def test_fake_quantize_in_place_matches_oracle(kv):
     rows, d, rpg = 9000, 128, 3000
     x = _x(rows, d, 5)
     xh = _u16(x)
@@ -114,11 +114,10 @@ def test_fake_quantize_in_place_matches_oracle(options):
         assert np.array_equal(_u16(xd).reshape(ofy.shape), ofy), rule
 
 
-def test_append_into_cache_slab_both_forms_agree(options):
+def test_append_into_cache_slab_both_forms_agree(kv):
     """A chunk appended into views of a larger cache (the benchmark's call pattern):
     the two forms write the same bytes, touch nothing outside the chunk's rows and group,
     and match the oracle."""
-    kv = options
     H, D, T, chunks = 12, 128, 1170, 4
     rpg = T * H
     rows = rpg * chunks
@@ -126,10 +125,11 @@ def test_append_into_cache_slab_both_forms_agree(options):
     src = _x(rpg, D, 12)
     out = {}
     for fused in (0, 1):
-        kv.kvfp4_set_option("append_fused", fused)
-        codes, scales, amax = kv.kvfp4_quantize(base.to(DEV), rpg, "mse")
+        opts = kv.quantize_opts("auto" if fused else "three_kernel")
+        codes, scales, amax = kv.kvfp4_quantize(base.to(DEV), rpg, "mse", opts=opts)
         last = slice(2 * rpg, 3 * rpg)
-        kv.kvfp4_quantize(src.to(DEV), rpg, "mse", codes[last], scales[last], amax[2:3])
+        kv.kvfp4_quantize(src.to(DEV), rpg, "mse", codes[last], scales[last], amax[2:3],
+                          opts=opts)
         torch.cuda.synchronize()
         out[fused] = (codes.cpu(), scales.cpu(), amax.cpu())
     for a, b in zip(out[0], out[1]):
@@ -142,12 +142,10 @@ def test_append_into_cache_slab_both_forms_agree(options):
     assert np.array_equal(out[1][2].numpy().view(np.uint32), oa.view(np.uint32))
 
 
-def test_concurrent_appends_on_two_streams(options):
+def test_concurrent_appends_on_two_streams(kv):
     """Two one-kernel appends enqueued back to back on two streams, so that they can run at
     the same time (different inputs and outputs): each call's hand-off lives in its own
     output, so both match the oracle."""
-    kv = options
-    kv.kvfp4_set_option("append_fused", 1)
     rows, d, rpg = 60000, 128, 6000
     xs = [_x(rows, d, 100 + i) for i in range(2)]
     streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]

@@ -21,6 +21,6 @@ def test_c_program_round_trip_matches_oracle():
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith("OK")
-    # 3 layouts x 3 rules x 2 quantize forms, 2 paged rules, 2 RTN widths
-    assert r.stdout.count("bit-exact") == 22
+    # 3 layouts x 3 rules x 2 quantize forms, the plain entry point, 2 paged rules, 2 RTN widths
+    assert r.stdout.count("bit-exact") == 23
     assert r.stdout.count("within tolerance") == 1

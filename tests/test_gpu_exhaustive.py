@@ -59,10 +59,11 @@ ARR = _arrangements()
 @pytest.fixture
 def options():
     import kv_cache_fp4_amd as kv
-    saved = {k: kv.kvfp4_get_option(k) for k in kv.OPTIONS}
-    yield kv
-    for k, v in saved.items():
-        kv.kvfp4_set_option(k, v)
+    return kv
+
+
+def _opts(kv, fused):
+    return kv.quantize_opts("auto" if fused else "three_kernel")
 
 
 def _u16(t):
@@ -73,13 +74,13 @@ def _u16(t):
 @pytest.mark.parametrize("name", list(ARR))
 def test_every_finite_bf16_pattern(options, name, fused):
     kv = options
-    kv.kvfp4_set_option("append_fused", fused)
+    opts = _opts(kv, fused)
     xh, rpg = ARR[name]
     x = torch.from_numpy(xh.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
     for rule in RULES:
-        c, s, a = kv.kvfp4_quantize(x, rpg, rule)
+        c, s, a = kv.kvfp4_quantize(x, rpg, rule, opts=opts)
         y = kv.kvfp4_dequantize(c, s, a, rpg)
-        fy, fa = kv.kvfp4_fake_quantize(x, rpg, rule)
+        fy, fa = kv.kvfp4_fake_quantize(x, rpg, rule, opts=opts)
         torch.cuda.synchronize()
         oc, os_, oa = oracle.quantize(xh, rpg, rule)
         what = (name, fused, rule)
@@ -99,7 +100,7 @@ def test_every_finite_bf16_pattern_paged(options, rows_per_page, fused):
     seeded random order (every page its own scale group, from subnormal-amax pages up), then
     gathered back to dense bf16 and float32."""
     kv = options
-    kv.kvfp4_set_option("append_fused", fused)
+    opts = _opts(kv, fused)
     xh = ARR["in_order/1"][0]
     n_blocks = xh.shape[0] // rows_per_page
     xh = xh[: n_blocks * rows_per_page]
@@ -111,7 +112,7 @@ def test_every_finite_bf16_pattern_paged(options, rows_per_page, fused):
         codes = torch.zeros((n_pages, rows_per_page, D // 2), dtype=torch.uint8, device=DEV)
         scales = torch.zeros((n_pages, rows_per_page, D // 16), dtype=torch.uint8, device=DEV)
         amax = torch.zeros((n_pages,), dtype=torch.float32, device=DEV)
-        kv.kvfp4_quantize_paged(x, td, rows_per_page, codes, scales, amax, rule)
+        kv.kvfp4_quantize_paged(x, td, rows_per_page, codes, scales, amax, rule, opts=opts)
         y = kv.kvfp4_dequantize_paged(codes, scales, amax, td, rows_per_page)
         y32 = kv.kvfp4_dequantize_paged_f32(codes, scales, amax, td, rows_per_page)
         torch.cuda.synchronize()

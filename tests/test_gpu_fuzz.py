@@ -78,10 +78,11 @@ def _case(seed):
 @pytest.fixture
 def options():
     import kv_cache_fp4_amd as kv
-    saved = {k: kv.kvfp4_get_option(k) for k in kv.OPTIONS}
-    yield kv
-    for k, v in saved.items():
-        kv.kvfp4_set_option(k, v)
+    return kv
+
+
+def _opts(kv, fused):
+    return kv.quantize_opts("auto" if fused else "three_kernel")
 
 
 def _u16(t):
@@ -98,11 +99,11 @@ def test_fuzz_matches_oracle(options, seed):
     oy32 = oracle.dequantize_f32(oc, os_, oa, rpg)
     ofy, ofa = oracle.fake_quantize(xh, rpg, rule)
     for fused in (1, 0):
-        kv.kvfp4_set_option("append_fused", fused)
-        c, s, a = kv.kvfp4_quantize(x, rpg, rule)
+        opts = _opts(kv, fused)
+        c, s, a = kv.kvfp4_quantize(x, rpg, rule, opts=opts)
         y = kv.kvfp4_dequantize(c, s, a, rpg)
         y32 = kv.kvfp4_dequantize_f32(c, s, a, rpg)
-        fy, fa = kv.kvfp4_fake_quantize(x, rpg, rule)
+        fy, fa = kv.kvfp4_fake_quantize(x, rpg, rule, opts=opts)
         torch.cuda.synchronize()
         what = (seed, xh.shape, rpg, rule, fused)
         assert np.array_equal(a.cpu().numpy().view(np.uint32), oa.view(np.uint32)), what

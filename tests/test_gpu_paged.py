@@ -18,21 +18,17 @@ def _u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.fixture
-def fused_option():
+def _opts(fused):
     import kv_cache_fp4_amd as kv
-    saved = kv.kvfp4_get_option("append_fused")
-    yield kv
-    kv.kvfp4_set_option("append_fused", saved)
+    return kv.quantize_opts("auto" if fused else "three_kernel")
 
 
 @pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
 @pytest.mark.parametrize("rule", ["static_6", "static_4", "mse"])
 @pytest.mark.parametrize("nb,rpp,d", [(37, 16 * 12, 128), (5, 64, 64), (200, 16 * 4, 256),
                                       (9, 1, 64)])
-def test_paged_round_trip_matches_oracle(fused_option, fused, rule, nb, rpp, d):
-    kv = fused_option
-    kv.kvfp4_set_option("append_fused", fused)
+def test_paged_round_trip_matches_oracle(fused, rule, nb, rpp, d):
+    import kv_cache_fp4_amd as kv
     npg = nb + 7
     x = synth.gauss_outliers((nb * rpp, d), seed=nb + rpp + d)
     tab = np.random.default_rng(nb).permutation(npg)[:nb].astype(np.int32)
@@ -40,7 +36,7 @@ def test_paged_round_trip_matches_oracle(fused_option, fused, rule, nb, rpp, d):
     scales = torch.full((npg, rpp, d // 16), 0x33, dtype=torch.uint8, device=DEV)
     amax = torch.full((npg,), -3.0, dtype=torch.float32, device=DEV)
     ttab = torch.from_numpy(tab).to(DEV)
-    kv.kvfp4_quantize_paged(x.to(DEV), ttab, rpp, codes, scales, amax, rule)
+    kv.kvfp4_quantize_paged(x.to(DEV), ttab, rpp, codes, scales, amax, rule, opts=_opts(fused))
     y = kv.kvfp4_dequantize_paged(codes, scales, amax, ttab, rpp)
     torch.cuda.synchronize()
     oc = np.full((npg, rpp, d // 2), 0x5A, np.uint8)
@@ -54,11 +50,10 @@ def test_paged_round_trip_matches_oracle(fused_option, fused, rule, nb, rpp, d):
 
 
 @pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
-def test_paged_quantize_skips_entries(fused_option, fused):
+def test_paged_quantize_skips_entries(fused):
     """Write-side table entries outside [0, n_pages) are skipped: their blocks write nothing
     and every page not named keeps its old bytes."""
-    kv = fused_option
-    kv.kvfp4_set_option("append_fused", fused)
+    import kv_cache_fp4_amd as kv
     nb, rpp, d, npg = 6, 192, 128, 5
     x = synth.gauss_outliers((nb * rpp, d), seed=11)
     tab = np.array([3, -1, 0, npg + 2, 1, 4], dtype=np.int32)
@@ -66,7 +61,7 @@ def test_paged_quantize_skips_entries(fused_option, fused):
     scales = torch.full((npg, rpp, d // 16), 0x33, dtype=torch.uint8, device=DEV)
     amax = torch.full((npg,), -3.0, dtype=torch.float32, device=DEV)
     kv.kvfp4_quantize_paged(x.to(DEV), torch.from_numpy(tab).to(DEV), rpp, codes, scales, amax,
-                            "mse")
+                            "mse", opts=_opts(fused))
     torch.cuda.synchronize()
     oc = np.full((npg, rpp, d // 2), 0x5A, np.uint8)
     os_ = np.full((npg, rpp, d // 16), 0x33, np.uint8)
