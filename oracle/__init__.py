@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.kvfp4_oracle_rtn_dequantize.argtypes = [P, P, i64, i32, i32, P]
         L.kvfp4_oracle_rtn_dequantize.restype = i32
         for name in ("kvfp4_oracle_e2m1_encode_n", "kvfp4_oracle_e4m3_encode_n",
-                     "kvfp4_oracle_float_to_bf16_n"):
+                     "kvfp4_oracle_float_to_bf16_n", "kvfp4_oracle_double_to_bf16_n"):
             getattr(L, name).argtypes = [P, i64, P]
             getattr(L, name).restype = None
         _lib = L
@@ -131,6 +131,14 @@ def float_to_bf16(f) -> np.ndarray:
     f = np.ascontiguousarray(f, dtype=np.float32).reshape(-1)
     out = np.empty(f.size, dtype=np.uint16)
     lib().kvfp4_oracle_float_to_bf16_n(_p(f), f.size, _p(out))
+    return out
+
+
+def double_to_bf16(f) -> np.ndarray:
+    """Round doubles to bf16 in one step (the attention output's rounding)."""
+    f = np.ascontiguousarray(f, dtype=np.float64).reshape(-1)
+    out = np.empty(f.size, dtype=np.uint16)
+    lib().kvfp4_oracle_double_to_bf16_n(_p(f), f.size, _p(out))
     return out
 
 

@@ -137,6 +137,28 @@ uint16_t kvfp4_oracle_float_to_bf16(float f) {
   return (uint16_t)(pick >> 16);
 }
 
+/* Round a double to the nearest bf16 value, ties to the even bf16 mantissa, in one step
+ * (no intermediate binary32 rounding).  bf16 has 8 significant bits above 2^-126 and a
+ * fixed spacing of 2^-133 below it; a magnitude that rounds to 2^128 or more overflows to
+ * infinity. */
+uint16_t kvfp4_oracle_double_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0u;
+  const uint16_t sign = signbit(v) ? 0x8000u : 0x0000u;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                                  /* a = f * 2^e, f in [0.5, 1) */
+  int q = e - 8;                                 /* spacing 2^q for 8 significant bits */
+  if (q < -133) q = -133;                        /* subnormal range: spacing 2^-133 */
+  double scaled = ldexp(a, -q);                  /* exact: a power-of-two scaling */
+  double k = floor(scaled);
+  double below = scaled - k, above = (k + 1.0) - scaled;   /* both exact */
+  if (above < below || (above == below && fmod(k, 2.0) != 0.0)) k += 1.0;
+  double r = ldexp(k, q);                        /* exact unless it overflows */
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+  return (uint16_t)(sign | (bits_from_f32((float)r) >> 16));  /* r is a bf16 value */
+}
+
 /* ------------------------------------------------------------------------------------
  * Quantization.  [P-NVFP4] "Stage 1" (per-block amax, per-block scale by the static-6
  * rule, two codes per uint8, one global amax for the whole tensor) and "Stage 3"
@@ -451,7 +473,8 @@ int kvfp4_oracle_rtn_dequantize(const uint8_t* codes, const uint16_t* scales, in
  * Attention over a dequantized cache.  [P-KV] "CUDA De-quantization Pipeline" (the bf16
  * K/V reconstructed before attention feed the attention operation); [P-SF] Table 3 (the
  * active cache is dequantized to dense BF16 before attention).  The operation itself is
- * the textbook one: O = softmax(scale * Q K^T) V per head, non-causal, here in double.
+ * the textbook one: O = softmax(scale * Q K^T) V per head, non-causal, here in double,
+ * with the double result rounded to bf16 once.
  * Layouts: q [tq, heads, d], k and v [tk, heads, d], all bf16; out [tq, heads, d] bf16.
  * Only the listed (token, head) query rows are computed: rows[i] = token * heads + head.
  * ---------------------------------------------------------------------------------- */
@@ -483,7 +506,7 @@ int kvfp4_oracle_attend_rows(const uint16_t* q, const uint16_t* k, const uint16_
       double o = 0.0;
       for (int64_t j = 0; j < tk; ++j)
         o += scratch[j] * (double)kvfp4_oracle_bf16_to_float(v[(j * heads + h) * d + c]);
-      out[i * d + c] = kvfp4_oracle_float_to_bf16((float)(o / den));
+      out[i * d + c] = kvfp4_oracle_double_to_bf16(o / den);   /* one rounding */
     }
   }
   return 0;
@@ -500,4 +523,7 @@ void kvfp4_oracle_e4m3_encode_n(const float* u, int64_t n, uint8_t* out) {
 }
 void kvfp4_oracle_float_to_bf16_n(const float* f, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = kvfp4_oracle_float_to_bf16(f[i]);
+}
+void kvfp4_oracle_double_to_bf16_n(const double* f, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvfp4_oracle_double_to_bf16(f[i]);
 }

@@ -109,6 +109,33 @@ def test_e4m3_encode_vs_torch_float8():
     assert np.array_equal(oracle.e4m3_encode(u), _torch_e4m3(u))
 
 
+def test_e4m3_encode_every_binary32_in_range():
+    """Brute force: every binary32 value in [2^-12, 2^10] (about 1.8e8 values, the whole range
+    a block scale's encode operand u takes in ordinary groups and then some).  Below 448 the
+    oracle's table scan equals torch's float8_e4m3fn conversion (an independent
+    implementation of round-to-nearest-even into OCP E4M3); from 448 up it saturates to
+    0x7E, the reading of the pages' FP8 block scale taken here (torch has no saturating
+    mode).  Chunks run on the host's threads (the oracle's C calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lo = int(_bits(np.float32(2.0 ** -12)))
+    hi = int(_bits(np.float32(2.0 ** 10)))
+    sat = int(_bits(np.float32(448.0)))
+    step = 1 << 22
+
+    def chunk(b0):
+        b = np.arange(b0, min(b0 + step, hi + 1), dtype=np.uint32)
+        u = _f32(b)
+        got = oracle.e4m3_encode(u)
+        below = b < sat
+        ok = np.array_equal(got[below], _torch_e4m3(u[below]))
+        return ok and bool(np.all(got[~below] == 0x7E)), int(b.size)
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        res = list(ex.map(chunk, range(lo, hi + 1, step)))
+    assert all(ok for ok, _ in res)
+    assert sum(n for _, n in res) == hi - lo + 1 == 22 * (1 << 23) + 1
+
+
 def test_e4m3_saturates_at_448():
     u = np.float32([448.0, 448.5, 463.9, 464.0, 1000.0, 3.0e38, np.inf])
     assert np.all(oracle.e4m3_encode(u) == 0x7E)

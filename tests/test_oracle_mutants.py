@@ -52,6 +52,10 @@ MUTANTS = {
     "rtn scale kept in fp32": ("uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);\n      float sv = kvfp4_oracle_bf16_to_float(sh);",
                                "uint16_t sh = kvfp4_oracle_float_to_bf16(m / (float)qmax);\n      float sv = m / (float)qmax;"),
     "rtn dequant drops sign": ("int q = (raw >= (1 << (bits - 1))) ? raw - (1 << bits) : raw;", "int q = raw;"),
+    "attention output rounded through binary32": (
+        "kvfp4_oracle_double_to_bf16(o / den);", "kvfp4_oracle_float_to_bf16((float)(o / den));"),
+    "double to bf16 ties up": ("if (above < below || (above == below && fmod(k, 2.0) != 0.0)) k += 1.0;",
+                               "if (above <= below) k += 1.0;"),
     "attention keys off by one": ("const uint16_t* kr = k + (j * heads + h) * d;",
                                   "const uint16_t* kr = k + (((j + 1) % tk) * heads + h) * d;"),
 }
@@ -70,7 +74,9 @@ def test_pins_catch_planted_mistake(name):
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                         "-o", so, c, "-lm"], check=True, capture_output=True)
         env = dict(os.environ, KVFP4_ORACLE_LIB=so)
+        # the E4M3 brute force (~30 s) is left out here: the E4M3 mutants are caught by the
+        # midpoint sweeps, and it would otherwise run once per mutant
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            *PIN_TESTS], cwd=ROOT, env=env, capture_output=True, text=True,
-                           timeout=600)
+                            "-k", "not every_binary32", *PIN_TESTS], cwd=ROOT, env=env,
+                           capture_output=True, text=True, timeout=600)
         assert r.returncode != 0, f"no pin failed for planted mistake: {name}\n{r.stdout[-2000:]}"
