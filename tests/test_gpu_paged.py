@@ -94,22 +94,49 @@ def test_paged_gather_skips_and_repeats():
     assert np.array_equal(y.cpu().numpy().view(np.uint16), want)
 
 
-def test_full_size_paged_cache_sampled():
+def test_full_size_paged_cache_every_page():
     """30 layers x K,V x 2048 pages of 16 tokens (32768 tokens) x 12 heads x 128, pages in a
-    random physical order; 6 sampled pages recomputed by the oracle from the same inputs."""
+    random physical order: all 122,880 pages (codes, scale bytes, page amax) and the whole
+    gather to dense bf16, bit for bit against the oracle, which quantizes and gathers the
+    same blocks through the same table on the host's threads (each thread a run of blocks;
+    the table is a permutation, so their pages are disjoint)."""
+    import os
+    import time
+    from concurrent.futures import ThreadPoolExecutor
+
     import bench
+    t0 = time.perf_counter()
     w = bench.PagedWorkload(DEV)
     w.dequantize_all()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(11)
     tab = w.table.cpu().numpy()
-    for b in [0, w.n_blocks - 1] + list(rng.integers(0, w.n_blocks, 4)):
-        r0 = int(b) * w.rpp
-        xb = _u16(w.src[r0:r0 + w.rpp])
-        pg = int(tab[b])
-        oc, os_, oa = oracle.quantize_paged(xb, np.array([0], np.int32), w.rpp, 1, "static_6")
-        assert np.array_equal(w.codes[pg].cpu().numpy(), oc[0])
-        assert np.array_equal(w.scales[pg].cpu().numpy(), os_[0])
-        assert w.amax[pg].item() == oa[0]
-        assert np.array_equal(_u16(w.out[r0:r0 + w.rpp]),
-                              oracle.dequantize_rows(oc[0], os_[0], oa[0]))
+    assert np.array_equal(np.sort(tab), np.arange(w.n_blocks))
+    xh = _u16(w.src)
+    D = xh.shape[1]
+    oc = np.zeros((w.n_blocks, w.rpp, D // 2), np.uint8)
+    os_ = np.zeros((w.n_blocks, w.rpp, D // 16), np.uint8)
+    oa = np.zeros(w.n_blocks, np.float32)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    parts = np.array_split(np.arange(w.n_blocks), threads * 4)
+
+    def quant(p):
+        b0, b1 = int(p[0]), int(p[-1]) + 1
+        oracle.quantize_paged(xh[b0 * w.rpp:b1 * w.rpp], tab[b0:b1], w.rpp, w.n_blocks,
+                              "static_6", oc, os_, oa)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(quant, parts))
+    assert np.array_equal(w.codes.cpu().numpy(), oc)
+    assert np.array_equal(w.scales.cpu().numpy(), os_)
+    assert np.array_equal(w.amax.cpu().numpy().view(np.uint32), oa.view(np.uint32))
+    gy = _u16(w.out)
+
+    def gather_ok(p):
+        b0, b1 = int(p[0]), int(p[-1]) + 1
+        oy = oracle.dequantize_paged(oc, os_, oa, tab[b0:b1], w.rpp)
+        return np.array_equal(gy[b0 * w.rpp:b1 * w.rpp], oy)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        assert all(ex.map(gather_ok, parts))
+    print(f"paged cache: {w.n_blocks} pages checked in {time.perf_counter() - t0:.1f} s on "
+          f"{threads} threads")
