@@ -54,6 +54,9 @@ def parse_args(argv=None):
                     help="skip the float32-output dequantize and fake-quantize timings")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip the fused dequantize+attention timing (reported beside the step)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the one-layer chunk append and the 5B-shaped rollout step "
+                         "(reported beside the step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args(argv)
@@ -229,6 +232,87 @@ def bench_rtn(device, steps=20, warmup=3):
                                         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
         del codes, scales
     del x, out
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---- the other configurations: one-layer chunk append, 5B-shaped rollout step ----------------
+
+MALL_BYTES = 1 << 30  # buffer sets rotated over at least this many bytes (Infinity Cache: 256 MB)
+
+
+def bench_chunk_append(device, calls=300, warmup=30):
+    """One layer's chunk append: K and V [4680, 12, 128] bf16 quantized with static_6 (one
+    scale group per tensor, one quantize call for both).  Each call reads its own copy of the
+    input and writes its own outputs, rotating over sets that total >= 1 GiB, so neither the
+    input nor the outputs are served from the Infinity Cache.  Algorithmic bytes per call:
+    14,376,960 elements x 2.5625 + 4 per group; the rate includes the call's three kernel
+    launches."""
+    import torch
+
+    import kv_cache_fp4_amd as kv
+    import synth
+    cfg = synth.C2
+    x0 = torch.cat([synth.chunk_group(cfg, 0, kv_, 0, device=device).reshape(-1, cfg.head_dim)
+                    for kv_ in (0, 1)])
+    rows, D, rpg = x0.shape[0], cfg.head_dim, cfg.rows_per_group
+    nbytes = rows * D * BYTES_PER_ELEM + 4 * 2
+    n_sets = -(-MALL_BYTES // int(nbytes))
+    sets = [(x0.clone(), torch.empty((rows, D // 2), dtype=torch.uint8, device=device),
+             torch.empty((rows, D // 16), dtype=torch.uint8, device=device),
+             torch.empty((2,), dtype=torch.float32, device=device)) for _ in range(n_sets)]
+    k = [0]
+
+    def call():
+        x, c, sc, a = sets[k[0] % n_sets]
+        k[0] += 1
+        kv.kvfp4_quantize(x, rpg, "static_6", c, sc, a)
+
+    for _ in range(warmup):
+        call()
+    ms = _time_calls(lambda: [call() for _ in range(calls)], device, 3, 0) / calls
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": (f"{cfg.name}: quantize one {cfg.chunk_tokens}-token chunk of one layer's K "
+                        f"and V ({cfg.heads} heads x {cfg.head_dim}, static_6, one group per "
+                        f"tensor), {n_sets} rotating buffer sets ({n_sets * nbytes / 2**30:.2f} GiB)"),
+           "us_per_call": round(ms * 1e3, 2), "bytes_per_call": nbytes,
+           "GBps": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    del sets, x0
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_rollout_5b(device, steps=10, warmup=3):
+    """5B-shaped rollout step: 30 layers, 24 heads, head_dim 128, a 36,960-token cache in 14
+    chunks of 2,640 tokens (static_6).  Appending one chunk for every layer's K and V under
+    each of static_6, static_4 and mse (one quantize call each), and dequantizing the whole
+    cache (one call).  Per rule: the append, and the step = append + whole-cache dequantize."""
+    import torch
+
+    import synth
+    cfg = synth.C4
+    w = CacheWorkload(cfg, "static_6", device)
+    dq_ms = _time_calls(w.dequantize_all, device, steps, warmup)
+    dq_bytes = w.dequant_bytes()
+    res = {"workload": (f"{cfg.name}: append one {cfg.chunk_tokens}-token chunk for {cfg.layers} "
+                        f"layers x K,V ({cfg.heads} heads x {cfg.head_dim}) + dequantize the whole "
+                        f"{cfg.cache_tokens}-token cache"),
+           "dequantize": {"ms": round(dq_ms, 4), "bytes": dq_bytes,
+                          "GBps": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 2),
+                          "pct_of_hbm_peak": round(100 * dq_bytes / (dq_ms * 1e-3) / 1e9
+                                                   / HBM_PEAK_GBS, 2)}}
+    for rule in ("static_6", "static_4", "mse"):
+        w.rule = rule
+        ap_ms = _time_calls(w.append, device, steps, warmup)
+        ap_bytes = w.append_bytes()
+        step_gbs = (ap_bytes + dq_bytes) / ((ap_ms + dq_ms) * 1e-3) / 1e9
+        res[rule] = {"append_ms": round(ap_ms, 4), "append_bytes": ap_bytes,
+                     "append_GBps": round(ap_bytes / (ap_ms * 1e-3) / 1e9, 2),
+                     "append_pct_of_hbm_peak": round(100 * ap_bytes / (ap_ms * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBS, 2),
+                     "step_ms": round(ap_ms + dq_ms, 4), "step_GBps": round(step_gbs, 2),
+                     "step_pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2)}
+    del w
     torch.cuda.empty_cache()
     return res
 
@@ -569,6 +653,13 @@ def main(argv=None):
     if not args.no_f32_fake:
         print("bench: timing float32 dequantize and fake quantize", file=sys.stderr, flush=True)
         res.update(bench_f32_fake(w, dev))
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        print("bench: timing the one-layer chunk append and the 5B-shaped rollout step",
+              file=sys.stderr, flush=True)
+        res["chunk_append"] = bench_chunk_append(dev)
+        res["rollout_5b"] = bench_rollout_5b(dev)
     if not args.no_rtn:
         print("bench: timing the RTN INT4/INT2 caches", file=sys.stderr, flush=True)
         res["rtn"] = bench_rtn(dev)
