@@ -89,11 +89,11 @@ enum kvfp4_rule {
  *   scales  (out)   uint8 [rows, head_dim/16]; 4-byte aligned
  *   group_amax (out) float [ceil(rows/rows_per_group)]; 4-byte aligned
  * Appending a chunk to a cache = passing pointers offset to the chunk's first row and
- * group.  Inputs must be finite.  Enqueues three kernels: when every group (the last one
- * included) has at least 528 elements, a hand-off clear, one kernel that computes the group
- * amax and encodes (it borrows three dwords of each group's codes for the hand-off; the
- * codes are complete when the call's work ends), and a finish kernel; otherwise amax
- * clear, group amax, encode.  Both give the same bytes.  (These are the default options of
+ * group.  Inputs must be finite.  Enqueues three kernels: for inputs of at least 40 MiB
+ * (80 MiB under mse) whose every group (the last one included) has at least 528 elements, a
+ * hand-off clear, one kernel that computes the group amax and encodes (it borrows three
+ * dwords of each group's codes for the hand-off; the codes are complete when the call's work
+ * ends), and a finish kernel; otherwise amax clear, group amax, encode.  Both give the same bytes.  (These are the default options of
  * kvfp4_quantize_ex, below.)
  */
 int kvfp4_quantize(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rows_per_group,
@@ -246,10 +246,14 @@ int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
  * kvfp4_fake_quantize_ex enqueue their work.  They never change an output byte.  [P-KV]
  * "Programmatic Configuration" carries its settings in a configuration object handed to the
  * call that uses them; these options travel the same way (no process-wide settings).
- *   form     KVFP4_FORM_AUTO (the default): one kernel computes the group amax and encodes
- *            wherever that applies (not in place, every group -- the last one included --
- *            at least 528 elements, 32-bit grid); otherwise three kernels (clear the amax
- *            words, group amax, encode).  KVFP4_FORM_THREE_KERNEL: always three kernels.
+ *   form     KVFP4_FORM_ONE_KERNEL: one kernel computes the group amax and encodes wherever
+ *            that applies (not in place, every group -- the last one included -- at least
+ *            528 elements, 32-bit grid); otherwise three kernels (clear the amax words,
+ *            group amax, encode).  KVFP4_FORM_THREE_KERNEL: always three kernels.
+ *            KVFP4_FORM_AUTO (the default): the one-kernel form where it applies and the
+ *            call's input holds at least 40 MiB of bf16 (80 MiB under the mse rule), else
+ *            three kernels -- the measured crossover: below it the three passes, each at
+ *            full parallelism, finish first.
  *   wait_us  in the one-kernel form, the longest time in microseconds an encode workgroup
  *            waits for its group amax before it computes the amax itself from the input
  *            (the same value); 0 = never wait; default 20000; at most 60000000.
@@ -259,7 +263,8 @@ int kvfp4_packed_sizes(int64_t rows, int32_t head_dim, int64_t rows_per_group,
  */
 enum kvfp4_form {
   KVFP4_FORM_AUTO = 0,
-  KVFP4_FORM_THREE_KERNEL = 1
+  KVFP4_FORM_THREE_KERNEL = 1,
+  KVFP4_FORM_ONE_KERNEL = 2
 };
 struct kvfp4_quantize_opts {
   int32_t form;     /* enum kvfp4_form */

@@ -24,7 +24,7 @@ RULES = {"static_6": 0, "static_4": 1, "mse": 2}
 KVFP4_OK, KVFP4_EINVAL, KVFP4_EALIGN, KVFP4_EUNSUPPORTED, KVFP4_EHIP = range(5)
 
 
-FORMS = {"auto": 0, "three_kernel": 1}
+FORMS = {"auto": 0, "three_kernel": 1, "one_kernel": 2}
 
 
 class QuantizeOpts(ctypes.Structure):
@@ -33,7 +33,8 @@ class QuantizeOpts(ctypes.Structure):
 
 
 def quantize_opts(form="auto", wait_us: int = 20000) -> QuantizeOpts:
-    """Options for the quantize calls: ``form`` "auto" (one kernel where it applies) or
+    """Options for the quantize calls: ``form`` "auto" (one kernel where it applies and the
+    input is large enough for it to be faster), "one_kernel" (wherever it applies) or
     "three_kernel"; ``wait_us`` bounds the one-kernel form's wait for a group amax."""
     return QuantizeOpts(FORMS[form] if isinstance(form, str) else int(form), int(wait_us))
 

@@ -824,7 +824,9 @@ constexpr int64_t kMaxWaitUs = INT64_C(60000000);
 int read_opts(const kvfp4_quantize_opts* in, kvfp4_quantize_opts* out) {
   const kvfp4_quantize_opts def = KVFP4_QUANTIZE_OPTS_DEFAULT;
   *out = in ? *in : def;
-  if (out->form != KVFP4_FORM_AUTO && out->form != KVFP4_FORM_THREE_KERNEL) return KVFP4_EINVAL;
+  if (out->form != KVFP4_FORM_AUTO && out->form != KVFP4_FORM_THREE_KERNEL &&
+      out->form != KVFP4_FORM_ONE_KERNEL)
+    return KVFP4_EINVAL;
   if (out->wait_us < 0 || out->wait_us > kMaxWaitUs) return KVFP4_EINVAL;
   return KVFP4_OK;
 }
@@ -888,13 +890,20 @@ int launch_append(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg
 
 // Shared body of the dense, paged and fake quantize entry points (arguments and options
 // already checked).  With fake_y set, the encode pass writes bf16 there instead of
-// codes/scales.  Not-in-place calls take the one-launch append where it applies (and the
-// options allow); the rest take three kernels: clear, group amax, encode.
+// codes/scales.  Not-in-place calls take the one-launch append where it applies and the
+// options choose it; the rest take three kernels: clear, group amax, encode.
 int quantize_impl(const uint16_t* x, int64_t rows, int32_t head_dim, int64_t rpg, int32_t rule,
                   const int32_t* table, int64_t n_pages, uint8_t* codes, uint8_t* scales,
                   float* group_amax, uint16_t* fake_y, const kvfp4_quantize_opts& o,
                   hipStream_t s) {
-  if ((const void*)fake_y != (const void*)x && o.form == KVFP4_FORM_AUTO) {
+  // KVFP4_FORM_AUTO: the one-kernel form for inputs of at least 40 MiB (80 MiB under mse);
+  // below those sizes the three-kernel form measured faster (a chunk that fits inside the
+  // amax/encode lag leaves the one-kernel form's hand-off serialized, plus its finish kernel).
+  const int64_t in_bytes = rows * (int64_t)head_dim * 2;
+  const int64_t min_bytes = (rule == KVFP4_RULE_MSE ? INT64_C(80) : INT64_C(40)) << 20;
+  const bool one = o.form == KVFP4_FORM_ONE_KERNEL ||
+                   (o.form == KVFP4_FORM_AUTO && in_bytes >= min_bytes);
+  if ((const void*)fake_y != (const void*)x && one) {
     bool used = false;
     int arc;
     switch (rule) {

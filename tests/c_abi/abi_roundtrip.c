@@ -299,7 +299,7 @@ int main(void) {
   CHECK_HIP(hipStreamCreate(&st));
   int bad = 0;
   /* both quantize forms (the one-kernel form applies to the first and third layouts) */
-  const struct kvfp4_quantize_opts forms[2] = {KVFP4_QUANTIZE_OPTS_DEFAULT,
+  const struct kvfp4_quantize_opts forms[2] = {{KVFP4_FORM_ONE_KERNEL, 20000},
                                                {KVFP4_FORM_THREE_KERNEL, 20000}};
   for (int f = 0; f < 2; ++f) {
     printf("append form: %s\n", f == 0 ? "one kernel where it applies" : "three kernels");

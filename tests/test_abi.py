@@ -251,7 +251,7 @@ def qx(opts, **kw):
 
 
 @pytest.mark.parametrize("form,wait,want", [
-    (2, 20000, KVFP4_EINVAL), (-1, 20000, KVFP4_EINVAL), (0, -1, KVFP4_EINVAL),
+    (3, 20000, KVFP4_EINVAL), (-1, 20000, KVFP4_EINVAL), (0, -1, KVFP4_EINVAL),
     (1, 60000001, KVFP4_EINVAL), (0, 1 << 40, KVFP4_EINVAL),
 ])
 def test_quantize_options_rejected_per_call(form, wait, want):
@@ -263,7 +263,8 @@ def test_quantize_options_rejected_per_call(form, wait, want):
     assert lib.kvfp4_fake_quantize_ex(A16, 64, 128, 64, 0, A16, A16, o, None) == want
 
 
-@pytest.mark.parametrize("form,wait", [(0, 0), (0, 20000), (1, 0), (1, 60000000)])
+@pytest.mark.parametrize("form,wait", [(0, 0), (0, 20000), (1, 0), (1, 60000000), (2, 0),
+                                       (2, 20000)])
 def test_quantize_options_accepted(form, wait):
     """Valid options with zero rows: accepted, nothing to do (no device needed)."""
     o = ctypes.byref(kv.QuantizeOpts(form, wait))

@@ -67,11 +67,11 @@ def kv():
 
 
 def _form_opts(kv, form):
-    return kv.quantize_opts("three_kernel" if form == "three_kernels" else "auto",
-                            0 if form == "one_kernel_no_wait" else 20000)
+    name = {"three_kernels": "three_kernel", "auto": "auto"}.get(form, "one_kernel")
+    return kv.quantize_opts(name, 0 if form == "one_kernel_no_wait" else 20000)
 
 
-@pytest.mark.parametrize("form", ["one_kernel", "three_kernels", "one_kernel_no_wait"])
+@pytest.mark.parametrize("form", ["one_kernel", "three_kernels", "one_kernel_no_wait", "auto"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{d}/{g}" for r, d, g in SHAPES])
 def test_quantize_forms_match_oracle(kv, shape, form):
     opts = _form_opts(kv, form)
@@ -125,7 +125,7 @@ def test_append_into_cache_slab_both_forms_agree(kv):
     src = _x(rpg, D, 12)
     out = {}
     for fused in (0, 1):
-        opts = kv.quantize_opts("auto" if fused else "three_kernel")
+        opts = kv.quantize_opts("one_kernel" if fused else "three_kernel")
         codes, scales, amax = kv.kvfp4_quantize(base.to(DEV), rpg, "mse", opts=opts)
         last = slice(2 * rpg, 3 * rpg)
         kv.kvfp4_quantize(src.to(DEV), rpg, "mse", codes[last], scales[last], amax[2:3],

@@ -82,7 +82,7 @@ def options():
 
 
 def _opts(kv, fused):
-    return kv.quantize_opts("auto" if fused else "three_kernel")
+    return kv.quantize_opts("one_kernel" if fused else "three_kernel")
 
 
 def _u16(t):

@@ -1,8 +1,9 @@
 """The library under HIP graph capture: the entry points allocate nothing, never synchronize
 and clear the group amax words with a kernel (no memset node), so an append + whole-cache
-read + fused attention can be captured once and replayed.  Each replay gets new input
-values (copied into the captured buffers between replays, with eager work and a
-synchronization in between) and must match the eager result for those values bit for bit.
+read + fused attention can be captured once and replayed, with the append in either quantize
+form.  Each replay gets new input values (copied into the captured buffers between replays,
+with eager work and a synchronization in between) and must match the eager result for those
+values bit for bit.
 """
 import numpy as np
 import pytest
@@ -20,8 +21,10 @@ def _x(rows, d, seed):
         torch.bfloat16)
 
 
-def test_capture_append_read_attend_and_replay():
+@pytest.mark.parametrize("form", ["one_kernel", "three_kernel"])
+def test_capture_append_read_attend_and_replay(form):
     import kv_cache_fp4_amd as kv
+    opts = kv.quantize_opts(form)
     H, D, tpg, chunks = 4, 128, 300, 3
     rpg = tpg * H
     rows = rpg * chunks
@@ -36,7 +39,8 @@ def test_capture_append_read_attend_and_replay():
     last = slice((chunks - 1) * rpg, rows)
 
     def step():
-        kv.kvfp4_quantize(src, rpg, "mse", codes[last], scales[last], amax[chunks - 1:])
+        kv.kvfp4_quantize(src, rpg, "mse", codes[last], scales[last], amax[chunks - 1:],
+                          opts=opts)
         kv.kvfp4_dequantize(codes, scales, amax, rpg, y=y)
         kv.kvfp4_attend(q, codes, scales, amax, vc, vs, va, tpg, D ** -0.5, out=att)
 

@@ -20,7 +20,7 @@ def _u16(t):
 
 def _opts(fused):
     import kv_cache_fp4_amd as kv
-    return kv.quantize_opts("auto" if fused else "three_kernel")
+    return kv.quantize_opts("one_kernel" if fused else "three_kernel")
 
 
 @pytest.mark.parametrize("fused", [1, 0], ids=["one_kernel", "three_kernels"])
