@@ -11,8 +11,8 @@
 // Both conversions round to nearest, ties to even, and saturate at the largest finite value.
 //
 // gfx950 has single-instruction conversions between packed fp32 pairs and packed E2M1
-// (v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4) and from an fp32 pair to a bf16
-// pair (v_cvt_pk_bf16_f32).  Their "scale" operand only carries a power of two in the fp32
+// (v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4), from an fp32 pair to OCP E4M3
+// (v_cvt_pk_fp8_f32) and from an fp32 pair to a bf16 pair (v_cvt_pk_bf16_f32).  Their "scale" operand only carries a power of two in the fp32
 // exponent, so the NVFP4 block scale cannot ride on it: it is always 1.0 here and the block
 // scale is applied with an explicit binary32 multiply, which keeps the op order fixed.
 #pragma once
@@ -55,19 +55,11 @@ __device__ __forceinline__ uint32_t absmax8_bits(uint4 v) {
 // ---- FP8 E4M3 block scales --------------------------------------------------------------
 
 // u >= 0 and finite (NaN is outside the contract).  Nearest E4M3 byte, ties to even;
-// u >= 448 gives 0x7E.
+// u >= 448 gives 0x7E.  gfx950's fp32 -> fp8 conversion is OCP E4M3 (bias 7, subnormals,
+// round to nearest even); clamping to 448 first keeps it away from its overflow handling.
 __device__ __forceinline__ uint32_t e4m3_encode(float u) {
-  if (!(u < 448.0f)) return 0x7Eu;
-  // Subnormal range (u < 2^-6): the value is k * 2^-9 with k = rne(u * 512); k = 8 is the
-  // smallest normal, whose byte is also 8.  u * 512 is exact.
-  if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);
-  // Normal range: keep exponent and the top 3 mantissa bits, round the 20 dropped bits to
-  // nearest even; a carry out of the mantissa correctly bumps the exponent.
-  uint32_t b = __float_as_uint(u);
-  uint32_t q = (b >> 20) - (120u << 3);  // ((exp8 - 127 + 7) << 3) | mant[22:20]
-  uint32_t r = b & 0xFFFFFu;
-  q += (r > 0x80000u) | ((r == 0x80000u) & (q & 1u));
-  return q;  // <= 0x7E because u < 448
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(u, 448.0f), 0.0f, 0, false);
+  return (uint32_t)w & 0xFFu;
 }
 
 // Value of a non-negative E4M3 byte (0..0x7E), exact in binary32.
