@@ -7,8 +7,9 @@ Cases: shapes on both sides of the one-kernel form's applicability bound (every 
 the last included, at least 66 units of 8 elements), ragged last groups, many small groups,
 one large group, every head_dim class; guard bytes around each output; the one-kernel form
 with a zero wait bound (every encode workgroup that finds its group amax unpublished
-computes it itself: the failure path of the bounded wait, forced from the host); fake
-quantization in place (always three kernels) and not in place.
+computes it itself: the failure path of the bounded wait, forced from the host); the
+default form, which picks between the two by input size; fake quantization in place
+(always three kernels) and not in place.
 """
 import numpy as np
 import pytest
